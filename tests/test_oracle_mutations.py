@@ -1,0 +1,103 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case swaps one oracle helper for a plausibly wrong version and runs the
+pins that guard it; the pin must fail.  This shows the pins constrain the
+oracle rather than merely agree with it.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import pa_oracle as po
+from tests import test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        fn(*args)
+
+
+def test_swapped_block_and_offset_is_caught(monkeypatch, golden):
+    def wrong(bt_row, t, B):
+        t = np.asarray(t, np.int64)
+        return np.asarray(bt_row, np.int64)[t % B % len(bt_row)], t // B
+    monkeypatch.setattr(po, "logical_to_physical", wrong)
+    _fails(pins.test_address_examples, golden)
+
+
+def test_off_by_one_positions_are_caught(monkeypatch, golden):
+    monkeypatch.setattr(po, "token_positions",
+                        lambda n, q: np.arange(n - q + 1, n + 1, dtype=np.int64))
+    _fails(pins.test_varlen_examples, golden)
+    _fails(pins.test_address_examples, golden)
+
+
+def test_interleaved_gqa_map_is_caught(monkeypatch):
+    monkeypatch.setattr(po, "kv_head_of", lambda h, G: h % 3)
+    _fails(pins.test_decode_gqa_head_map)
+
+
+def test_missing_score_scale_is_caught(monkeypatch):
+    real = po.attend
+    monkeypatch.setattr(po, "attend", lambda q, K, V, s: real(q, K, V, 1.0))
+    _fails(pins.test_decode_matches_sdpa_contiguous, 4, 2, 64)
+
+
+def test_merge_without_rescale_is_caught(monkeypatch):
+    def wrong(m, l, O, num_parts):
+        R, H = m.shape[:2]
+        out = np.zeros((R, H, O.shape[-1]))
+        for r in range(R):
+            n = int(num_parts[r])
+            for h in range(H):
+                w = l[r, h, :n]                    # forgot e^{m_j - m}
+                out[r, h] = (w[:, None] * O[r, h, :n]).sum(0) / w.sum()
+        return out
+    monkeypatch.setattr(po, "merge_partitions", wrong)
+    _fails(pins.test_merge_equals_decode_and_is_order_free)
+
+
+def test_online_softmax_without_accumulator_rescale_is_caught(monkeypatch):
+    def wrong(q, K, V, scale, cuts):
+        sc = float(np.float32(scale))
+        m, l, A = -np.inf, 0.0, np.zeros(V.shape[1])
+        bounds = [0] + list(cuts) + [K.shape[0]]
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            S = (K[lo:hi] @ q) * sc
+            mn = max(m, S.max())
+            a = math.exp(m - mn) if m != -np.inf else 0.0
+            e = np.exp(S - mn)
+            l = a * l + e.sum()
+            A = A + e @ V[lo:hi]                   # forgot to rescale A
+            m = mn
+        return A / l
+    monkeypatch.setattr(po, "online_softmax_tiles", wrong)
+    _fails(pins.test_online_softmax_two_element_hand_case)
+
+
+def test_fnuz_fp8_bias_is_caught(monkeypatch):
+    def wrong(codes):
+        c = np.asarray(codes).astype(np.int64)
+        s = np.where(c & 0x80, -1.0, 1.0)
+        e, m = (c >> 3) & 0xF, c & 7
+        return np.where(e == 0, s * np.ldexp(m / 8.0, -7), s * np.ldexp(1 + m / 8.0, e - 8))
+    monkeypatch.setattr(po, "fp8_e4m3fn_to_f64", wrong)
+    _fails(pins.test_fp8_closed_form_all_codes)
+
+
+def test_top_left_causal_alignment_is_caught(monkeypatch):
+    monkeypatch.setattr(po, "token_positions",
+                        lambda n, q: np.arange(0, q, dtype=np.int64))
+    _fails(pins.test_prefill_chunks_compose)
+
+
+def test_gather_with_wrong_token_order_is_caught(monkeypatch):
+    def wrong(pool, bt_row, n, B):
+        t = np.arange(n, dtype=np.int64)
+        phys, off = po.logical_to_physical(bt_row, t, B)
+        return pool[phys, :, (B - 1 - off), :]     # reversed inside each block
+    monkeypatch.setattr(po, "gather_kv", wrong)
+    _fails(pins.test_decode_matches_sdpa_contiguous, 4, 2, 64)
+    _fails(pins.test_scatter_then_gather_roundtrip)
