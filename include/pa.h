@@ -1,0 +1,221 @@
+/*
+ * pa.h -- C ABI of libpa: paged attention over a block-table-addressed KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   [P1] "vLLM 深度解析（二）：PagedAttention 核心机制"
+ *   [P2] "第11章 分块预填充与混合批处理"
+ *   [P3] "vllm 深度解析：一切从 PagedAttention 谈起"
+ *   [P4] "LLM 推理基础与 vLLM 内部机制：KV 缓存、PagedAttention、调度器"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `layout`, `bytes_per_pool` and the host
+ *    arrays of pa_validate_metadata is a DEVICE pointer owned by the caller;
+ *    the library never allocates, frees or retains memory and keeps no state.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises the stream.
+ *  - Return value: PA_OK (0) on success, a negative pa_status otherwise.
+ *    Only host-visible arguments are checked (scalars, NULL pointers, 16-byte
+ *    alignment of K/V/Q/output buffers); on any error nothing is launched.
+ *  - Device metadata is trusted: block ids outside [0, num_blocks), slots
+ *    outside [0, num_blocks*block_size), seq_lens above bt_stride*block_size
+ *    or above the host limits (max_seq_len, max_query_len) are undefined
+ *    behaviour.  pa_validate_metadata checks host copies of the metadata.
+ *  - Block-table entries at or past ceil(seq_len / block_size) are never
+ *    read, whatever they hold.
+ *
+ * KV cache layout (chosen for 64-lane wavefronts; the pages' split
+ * x-interleaved K and dim-major V are not used):
+ *    k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ *  One (block, KV head) tile is block_size rows of head_dim contiguous
+ *  elements.  Element type: bf16 (raw 16-bit patterns) or OCP FP8 E4M3FN codes
+ *  (1 byte) with one fp32 scale per tensor, read from device memory.
+ *  Slot s (P1 §3.1: slot = physical_block * B + offset) is block s / B, row
+ *  s % B of every KV-head tile.
+ *
+ * Supported: block_size 16, head_dim 64 or 128, num_q_heads a multiple of
+ * num_kv_heads (query head h reads KV head h / (num_q_heads/num_kv_heads)).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* NULL / misaligned pointer, bad count or scalar */
+  PA_ERR_UNSUPPORTED = -2,  /* head_dim, block_size, dtype or head ratio not built */
+  PA_ERR_HIP = -3,          /* a HIP launch failed */
+  PA_ERR_METADATA = -4,     /* pa_validate_metadata found an inconsistency */
+};
+
+enum pa_cache_dtype {
+  PA_CACHE_BF16 = 0,
+  PA_CACHE_FP8_E4M3 = 1,    /* OCP E4M3FN, per-tensor fp32 scale */
+};
+
+typedef struct pa_kv_layout {
+  int32_t num_blocks;       /* physical blocks in each pool */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t block_size;       /* 16 */
+  int32_t cache_dtype;      /* enum pa_cache_dtype */
+} pa_kv_layout;
+
+/* Human-readable name of a status code (static string). */
+const char* pa_status_string(int status);
+
+/*
+ * Bytes of ONE pool (K or V) for `layout` (P1 §1 and P4 §2: per token the
+ * cache holds num_kv_heads * head_dim elements for K and as many for V).
+ * Host-only; writes *bytes_per_pool.
+ */
+int pa_kv_cache_bytes(const pa_kv_layout* layout, size_t* bytes_per_pool);
+
+/*
+ * Slot mapping (P1 §3.1 equations and the compute_slot_mapping listing;
+ * P3 _compute_slot_mappings_kernel).  For token j of request r, with
+ * q_len = query_start_loc[r+1] - query_start_loc[r] and
+ * pos = seq_lens[r] - q_len + (j - query_start_loc[r]):
+ *     slot_mapping[j] = block_table[r*bt_stride + pos/B] * B + pos % B.
+ *  slot_mapping    : int64 [num_tokens]            (output)
+ *  block_table     : int32 [num_reqs][bt_stride]
+ *  query_start_loc : int32 [num_reqs + 1], query_start_loc[num_reqs] == num_tokens
+ *  seq_lens        : int32 [num_reqs], K/V tokens visible this step, new ones included
+ */
+int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, int32_t num_reqs,
+                            int32_t num_tokens, int32_t block_size, void* stream);
+
+/*
+ * Scatter new K/V into the cache (P3 PagedAttention.write_to_paged_cache ->
+ * reshape_and_cache; P1 §3.1 table: slot_mapping writes the new tokens,
+ * block_table reads history).  Copies key[j][g][:] to k_cache slot
+ * slot_mapping[j], KV head g (and value likewise) bit for bit.  A negative
+ * slot skips token j.  Slots must be distinct.
+ *  key, value : bf16 [num_tokens][num_kv_heads][head_dim], contiguous
+ * Only PA_CACHE_BF16 layouts are accepted (quantising writes are not built).
+ */
+int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cache,
+                         const void* key, const void* value, int32_t num_tokens,
+                         const int64_t* slot_mapping, void* stream);
+
+/*
+ * Single-query decode attention (P1 §3.2: block-table walk, QK with GQA,
+ * masked tail, softmax, PV; P1 §2.2: exact result via the online-softmax
+ * state (m, l, A)).  For request r and query head h (g = h / G):
+ *     out[r][h] = softmax_t( scale * <q[r][h], K_r[t][g]> ) . V_r[t][g],
+ * t over 0 .. seq_lens[r]-1, K_r/V_r read through block_table row r.
+ * One pass per (request, KV head) -- no temporaries.  seq_lens[r] == 0
+ * gives a zero row.
+ *  out, q     : bf16 [num_reqs][num_q_heads][head_dim]
+ *  max_seq_len: host upper bound of seq_lens (grid sizing only)
+ *  scale      : softmax scale, e.g. 1/sqrt(head_dim)
+ *  k_scale, v_scale : device fp32 scalars, required for FP8 caches,
+ *                     ignored (may be NULL) for bf16
+ */
+int pa_decode(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+              int32_t num_q_heads, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+              int32_t max_seq_len, float scale, const float* k_scale,
+              const float* v_scale, void* stream);
+
+/*
+ * Split-KV decode, first stage (P1 §3.2.7 and §3.3, the V2 partitioning).
+ * Partition p of request r covers tokens [p*P, min((p+1)*P, seq_len)).
+ * For every partition p < ceil(seq_lens[r]/P) and query head h writes
+ *     max_logits[i] = max of scale*<q,k> over the partition (natural log units)
+ *     exp_sums[i]   = sum of exp(scale*<q,k> - max_logits[i])
+ *     tmp_out[i][:] = sum of exp(...) * v / exp_sums[i]   (fp32)
+ * with i = (r*num_q_heads + h)*max_num_partitions + p (the pages' V2 index).
+ * Other entries are not written.
+ *  partition_size : P, a positive multiple of block_size
+ *  max_num_partitions : row length of the partial arrays, >= ceil(max_seq_len/P)
+ *  tmp_out    : fp32 [num_reqs][num_q_heads][max_num_partitions][head_dim]
+ *  max_logits, exp_sums : fp32 [num_reqs][num_q_heads][max_num_partitions]
+ */
+int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
+                          int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                          const float* k_scale, const float* v_scale,
+                          int32_t partition_size, int32_t max_num_partitions,
+                          float* tmp_out, float* max_logits, float* exp_sums,
+                          void* stream);
+
+/*
+ * Split-KV decode, merge stage (P1 §3.2.9 equations):
+ *     m = max_j m_j,  L = sum_j l_j e^(m_j - m),
+ *     out = sum_j tmp_out_j * l_j e^(m_j - m) / L     -> bf16, round to nearest even
+ * over j < ceil(seq_lens[r] / partition_size).  Arguments as in
+ * pa_decode_partitioned; out is bf16 [num_reqs][num_q_heads][head_dim].
+ */
+int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits,
+                        const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
+                        int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                        int32_t max_num_partitions, void* stream);
+
+/*
+ * Varlen (chunked) prefill over the paged cache (P2 §11.6: query_start_loc
+ * as cu_seqlens_q, seq_lens as seqused_k, block_table for the paged K/V).
+ * Request r owns query rows query_start_loc[r] .. query_start_loc[r+1]-1;
+ * row i of it sits at position seq_lens[r] - q_len + i and attends keys
+ * 0 .. that position (causal).  Requests with q_len <= 1 take the decode
+ * path (P1 §5.2 split_decodes_and_prefills, threshold 1); q_len == 0 writes
+ * nothing.  The K/V of this step's tokens must already be in the cache
+ * (pa_reshape_and_cache first).
+ *  out, q : bf16 [num_tokens][num_q_heads][head_dim]
+ *  max_query_len, max_seq_len : host upper bounds (grid sizing only)
+ */
+int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q,
+                      int32_t num_tokens, int32_t num_q_heads, const void* k_cache,
+                      const void* v_cache, const int32_t* query_start_loc,
+                      const int32_t* seq_lens, const int32_t* block_table,
+                      int32_t bt_stride, int32_t num_reqs, int32_t max_query_len,
+                      int32_t max_seq_len, float scale, const float* k_scale,
+                      const float* v_scale, void* stream);
+
+/*
+ * Test support: gather the logical K and V of every request through the
+ * block table with the same addressing code the attention kernels use
+ * (P1 §3.1).  Row cu_seq_lens[r] + t of k_out/v_out is token t of request r.
+ *  k_out, v_out : [cu_seq_lens[num_reqs]][num_kv_heads][head_dim], cache dtype
+ *  cu_seq_lens  : int32 [num_reqs + 1], prefix sums of seq_lens
+ */
+int pa_debug_gather_kv(const pa_kv_layout* layout, void* k_out, void* v_out,
+                       const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, const int32_t* cu_seq_lens,
+                       int32_t num_reqs, int32_t max_seq_len, void* stream);
+
+/*
+ * Test support: decode n FP8 E4M3FN codes to fp32 with the conversion the
+ * attention kernels use.
+ */
+int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
+
+/*
+ * Host-side check of metadata the kernels trust.  All arrays are HOST
+ * pointers.  Checks: query_start_loc starts at 0 and is non-decreasing;
+ * 0 <= q_len <= seq_len; seq_len <= bt_stride*block_size; every block-table
+ * entry a request can read is in [0, num_blocks); when slot_mapping is not
+ * NULL, its non-negative entries are distinct and < num_blocks*block_size.
+ * Returns PA_OK or PA_ERR_METADATA (PA_ERR_INVALID_ARG for bad arguments).
+ */
+int pa_validate_metadata(const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                         int32_t num_reqs, const int64_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_blocks, int32_t block_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,217 @@
+"""paged_kv_cache_77_amd -- paged attention for MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/pa.h`` (``libpa.so``, built by
+``paged_kv_cache_77_amd.build``).  Each function has the C entry point's
+name; it marshals torch tensors (device memory) to pointers and launches on
+torch's current HIP stream.  All arithmetic runs in the HIP kernels: when
+the library is missing these functions raise, there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PA_CACHE_BF16", "PA_CACHE_FP8_E4M3", "PaError", "PaKvLayout", "lib", "make_layout",
+    "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
+    "pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_merge_partitions",
+    "pa_prefill_varlen", "pa_debug_gather_kv", "pa_debug_fp8_to_f32",
+    "pa_validate_metadata", "EXPORTED_SYMBOLS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_HIP = -3
+PA_ERR_METADATA = -4
+PA_CACHE_BF16 = 0
+PA_CACHE_FP8_E4M3 = 1
+
+EXPORTED_SYMBOLS = (
+    "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
+    "pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_merge_partitions",
+    "pa_prefill_varlen", "pa_debug_gather_kv", "pa_debug_fp8_to_f32",
+    "pa_validate_metadata",
+)
+
+
+class PaKvLayout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("cache_dtype", ctypes.c_int32)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {pa_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_77_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        lp = ctypes.POINTER(PaKvLayout)
+        sig = {
+            "pa_status_string": ([_I], ctypes.c_char_p),
+            "pa_kv_cache_bytes": ([lp, ctypes.POINTER(ctypes.c_size_t)], _I),
+            "pa_compute_slot_mapping": ([_P, _P, _I, _P, _P, _I, _I, _I, _P], _I),
+            "pa_reshape_and_cache": ([lp, _P, _P, _P, _P, _I, _P, _P], _I),
+            "pa_decode": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P], _I),
+            "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
+                                       _I, _I, _P, _P, _P, _P], _I),
+            "pa_merge_partitions": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+            "pa_prefill_varlen": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                   _F, _P, _P, _P], _I),
+            "pa_debug_gather_kv": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P], _I),
+            "pa_debug_fp8_to_f32": ([_P, _P, _I, _P], _I),
+            "pa_validate_metadata": ([_P, _I, _P, _P, _I, _P, _I, _I, _I], _I),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def make_layout(num_blocks: int, num_kv_heads: int, head_dim: int,
+                cache_dtype: int = PA_CACHE_BF16, block_size: int = 16) -> PaKvLayout:
+    return PaKvLayout(num_blocks, num_kv_heads, head_dim, block_size, cache_dtype)
+
+
+def _check(status: int, where: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def pa_kv_cache_bytes(layout: PaKvLayout) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_kv_cache_bytes(ctypes.byref(layout), ctypes.byref(n)), "pa_kv_cache_bytes")
+    return int(n.value)
+
+
+def pa_compute_slot_mapping(slot_mapping, block_table, query_start_loc, seq_lens,
+                            block_size: int = 16) -> None:
+    _check(lib().pa_compute_slot_mapping(
+        _dev(slot_mapping, "slot_mapping"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(query_start_loc, "query_start_loc"),
+        _dev(seq_lens, "seq_lens"), seq_lens.shape[0], slot_mapping.shape[0], block_size,
+        _stream()), "pa_compute_slot_mapping")
+
+
+def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping) -> None:
+    _check(lib().pa_reshape_and_cache(
+        ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(key, "key"), _dev(value, "value"), key.shape[0],
+        _dev(slot_mapping, "slot_mapping"), _stream()), "pa_reshape_and_cache")
+
+
+def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
+              scale: float, k_scale=None, v_scale=None) -> None:
+    _check(lib().pa_decode(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()), "pa_decode")
+
+
+def pa_decode_partitioned(layout, q, k_cache, v_cache, block_table, seq_lens,
+                          max_seq_len: int, scale: float, partition_size: int, tmp_out,
+                          max_logits, exp_sums, k_scale=None, v_scale=None) -> None:
+    _check(lib().pa_decode_partitioned(
+        ctypes.byref(layout), _dev(q, "q"), q.shape[0], q.shape[1], _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_table, "block_table"), block_table.shape[1],
+        _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale), _dev(k_scale, "k_scale"),
+        _dev(v_scale, "v_scale"), int(partition_size), max_logits.shape[2],
+        _dev(tmp_out, "tmp_out"), _dev(max_logits, "max_logits"), _dev(exp_sums, "exp_sums"),
+        _stream()), "pa_decode_partitioned")
+
+
+def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,
+                        partition_size: int) -> None:
+    _check(lib().pa_merge_partitions(
+        _dev(out, "out"), _dev(tmp_out, "tmp_out"), _dev(max_logits, "max_logits"),
+        _dev(exp_sums, "exp_sums"), _dev(seq_lens, "seq_lens"), seq_lens.shape[0],
+        out.shape[1], out.shape[2], int(partition_size), max_logits.shape[2], _stream()),
+        "pa_merge_partitions")
+
+
+def pa_prefill_varlen(layout, out, q, k_cache, v_cache, query_start_loc, seq_lens,
+                      block_table, max_query_len: int, max_seq_len: int, scale: float,
+                      k_scale=None, v_scale=None) -> None:
+    _check(lib().pa_prefill_varlen(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
+        _dev(block_table, "block_table"), block_table.shape[1], seq_lens.shape[0],
+        int(max_query_len), int(max_seq_len), float(scale), _dev(k_scale, "k_scale"),
+        _dev(v_scale, "v_scale"), _stream()), "pa_prefill_varlen")
+
+
+def pa_debug_gather_kv(layout, k_out, v_out, k_cache, v_cache, block_table, seq_lens,
+                       cu_seq_lens, max_seq_len: int) -> None:
+    _check(lib().pa_debug_gather_kv(
+        ctypes.byref(layout), _dev(k_out, "k_out"), _dev(v_out, "v_out"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), _dev(cu_seq_lens, "cu_seq_lens"),
+        seq_lens.shape[0], int(max_seq_len), _stream()), "pa_debug_gather_kv")
+
+
+def pa_debug_fp8_to_f32(codes, out) -> None:
+    _check(lib().pa_debug_fp8_to_f32(_dev(codes, "codes"), _dev(out, "out"), codes.numel(),
+                                     _stream()), "pa_debug_fp8_to_f32")
+
+
+def pa_validate_metadata(block_table, query_start_loc, seq_lens, slot_mapping,
+                         num_blocks: int, block_size: int = 16) -> int:
+    """Host check of metadata (numpy arrays); returns the status code."""
+    import numpy as np
+
+    def host(a, dt):
+        return None if a is None else np.ascontiguousarray(a, dtype=dt)
+    bt = host(block_table, np.int32)
+    qsl = host(query_start_loc, np.int32)
+    sl = host(seq_lens, np.int32)
+    sm = host(slot_mapping, np.int64)
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    return int(lib().pa_validate_metadata(
+        p(bt), bt.shape[1], p(qsl), p(sl), sl.shape[0], p(sm),
+        0 if sm is None else sm.shape[0], int(num_blocks), int(block_size)))

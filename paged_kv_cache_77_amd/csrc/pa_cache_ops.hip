@@ -1,0 +1,138 @@
+// Cache write path and addressing helpers of libpa (gfx950):
+//   slot mapping  -- "vLLM 深度解析（二）：PagedAttention 核心机制" §3.1
+//                    (slot = physical_block * B + offset); "vllm 深度解析：
+//                    一切从 PagedAttention 谈起" (_compute_slot_mappings_kernel)
+//   scatter       -- same page 3: write_to_paged_cache / reshape_and_cache
+//   debug gather  -- the read addressing of §3.1, exposed for bit-exact tests
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// One work-group per request; threads stride over the request's new tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ block_table,
+    int32_t bt_stride, const int32_t* __restrict__ query_start_loc,
+    const int32_t* __restrict__ seq_lens) {
+  const int r = blockIdx.x;
+  const int lo = query_start_loc[r];
+  const int hi = query_start_loc[r + 1];
+  const int first_pos = seq_lens[r] - (hi - lo);
+  const int32_t* row = block_table + (int64_t)r * bt_stride;
+  for (int j = lo + (int)threadIdx.x; j < hi; j += blockDim.x) {
+    const int pos = first_pos + (j - lo);
+    const int logical = pos / kBlock;
+    const int offset = pos - logical * kBlock;
+    slot_mapping[j] = (int64_t)row[logical] * kBlock + offset;
+  }
+}
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                               int32_t bt_stride, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, int32_t num_reqs,
+                               int32_t /*max_query_len_hint*/, hipStream_t stream) {
+  if (num_reqs == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_reqs), dim3(256), 0, stream,
+                     slot_mapping, block_table, bt_stride, query_start_loc, seq_lens);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte chunk of a (token, KV head) row, K and V together.
+// Rows are head_dim bf16 = 8 or 16 chunks; a tile row in the pool is the same
+// head_dim contiguous elements, so the copy is chunk for chunk.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    const int64_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim) {
+  const int chunks = head_dim / 8;                     // 16-byte chunks per row
+  const int64_t per_token = (int64_t)num_kv_heads * chunks;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per_token * num_tokens) return;
+  const int64_t j = i / per_token;
+  const int rem = (int)(i - j * per_token);
+  const int g = rem / chunks;
+  const int c = rem - g * chunks;
+  const int64_t slot = slot_mapping[j];
+  if (slot < 0) return;                                // padding token
+  const int64_t dst = slot_offset(slot, g, num_kv_heads, head_dim) / 8 + c;
+  k_cache[dst] = key[i];
+  v_cache[dst] = value[i];
+}
+
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key,
+                                    const void* value, int32_t num_tokens,
+                                    const int64_t* slot_mapping, int32_t num_kv_heads,
+                                    int32_t head_dim, hipStream_t stream) {
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     (uint4*)k_cache, (uint4*)v_cache, (const uint4*)key,
+                     (const uint4*)value, slot_mapping, num_tokens, num_kv_heads, head_dim);
+  return hipGetLastError();
+}
+
+// grid (ceil(max_seq_len/16), num_kv_heads, num_reqs); one row per token of
+// a block: threads copy 4-byte words of the row.
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    uint32_t* __restrict__ k_out, uint32_t* __restrict__ v_out,
+    const uint32_t* __restrict__ k_cache, const uint32_t* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_seq_lens,
+    int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes) {
+  const int r = blockIdx.z, g = blockIdx.y, b = blockIdx.x;
+  const int n = seq_lens[r];
+  if (b * kBlock >= n) return;
+  const int32_t phys = block_table[(int64_t)r * bt_stride + b];
+  const int words = head_dim * elem_bytes / 4;        // 4-byte words per row
+  const int64_t tile = tile_offset(phys, g, num_kv_heads, head_dim) * elem_bytes / 4;
+  for (int i = threadIdx.x; i < kBlock * words; i += blockDim.x) {
+    const int row = i / words, w = i - row * words;
+    const int t = b * kBlock + row;
+    if (t >= n) break;
+    const int64_t dst = (((int64_t)cu_seq_lens[r] + t) * num_kv_heads + g) * words + w;
+    k_out[dst] = k_cache[tile + (int64_t)row * words + w];
+    v_out[dst] = v_cache[tile + (int64_t)row * words + w];
+  }
+}
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* cu_seq_lens, int32_t num_reqs,
+                            int32_t max_seq_len, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t elem_bytes, hipStream_t stream) {
+  if (num_reqs == 0 || max_seq_len == 0) return hipSuccess;
+  dim3 grid((max_seq_len + kBlock - 1) / kBlock, num_kv_heads, num_reqs);
+  hipLaunchKernelGGL(gather_kv_kernel, grid, dim3(256), 0, stream, (uint32_t*)k_out,
+                     (uint32_t*)v_out, (const uint32_t*)k_cache, (const uint32_t*)v_cache,
+                     block_table, bt_stride, seq_lens, cu_seq_lens, num_kv_heads, head_dim,
+                     elem_bytes);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fp8_to_f32_kernel(const uint8_t* __restrict__ codes,
+                                                         float* __restrict__ out, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base = i * 4;
+  if (base >= n) return;
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k)
+    if (base + k < n) w |= (uint32_t)codes[base + k] << (8 * k);
+  const f32x4_t v = fp8x4_to_f32(w);
+  const float vals[4] = {v.x, v.y, v.z, v.w};
+  for (int k = 0; k < 4; ++k)
+    if (base + k < n) out[base + k] = vals[k];
+}
+
+hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
+                             hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int threads = (n + 3) / 4;
+  hipLaunchKernelGGL(fp8_to_f32_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream,
+                     codes, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace pa

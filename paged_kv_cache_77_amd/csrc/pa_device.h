@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels of libpa.
+//
+// Cache tiles: pool[num_blocks][num_kv_heads][16][head_dim]; one
+// (block, KV head) tile is 16 rows of head_dim contiguous elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 16;   // tokens per cache block
+constexpr int kWave = 64;    // CDNA wavefront
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// addressing (logical token -> physical tile): used by every kernel that
+// reads the cache and by the debug gather, so tests of the gather exercise
+// the kernels' own arithmetic.
+
+// Element offset of the (physical block, KV head) tile.  int64: pools exceed
+// 2^31 elements.
+__device__ __forceinline__ int64_t tile_offset(int32_t phys, int g, int num_kv_heads,
+                                               int head_dim) {
+  return ((int64_t)phys * num_kv_heads + g) * (int64_t)(kBlock * head_dim);
+}
+
+// Element offset of cache slot `slot` (block slot/16, row slot%16), KV head g.
+__device__ __forceinline__ int64_t slot_offset(int64_t slot, int g, int num_kv_heads,
+                                               int head_dim) {
+  const int64_t blk = slot / kBlock;
+  const int row = (int)(slot - blk * kBlock);
+  return tile_offset((int32_t)blk, g, num_kv_heads, head_dim) + (int64_t)row * head_dim;
+}
+
+// ---------------------------------------------------------------------------
+// conversions
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Four OCP E4M3FN codes packed in a word -> four floats (gfx950 hardware
+// conversion; its results for all 256 codes are checked by a GPU test).
+__device__ __forceinline__ f32x4_t fp8x4_to_f32(uint32_t w) {
+  f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Two floats -> packed bf16 pair (exact for values representable in bf16,
+// such as decoded FP8).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane moves (DPP within 16-lane rows; ds_bpermute across rows)
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;   // rotate right by 4 within 16 lanes
+constexpr int kRowRor8 = 0x128;   // rotate right by 8 within 16 lanes (== xor 8)
+
+__device__ __forceinline__ float xor_lanes(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace pa

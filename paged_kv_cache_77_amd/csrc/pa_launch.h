@@ -1,0 +1,79 @@
+// Kernel launchers of libpa (internal; the C ABI in pa_api.cpp validates
+// arguments and calls these).  Each returns a hipError_t from the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const void* q;             // bf16 rows
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;   // NULL: q/out row r is request r
+  const float* k_scale;             // NULL for bf16 caches
+  const float* v_scale;
+  void* out;                        // bf16, final output (NULL in partitioned mode)
+  float* tmp_out;                   // partitioned mode only
+  float* max_logits;
+  float* exp_sums;
+  int32_t num_reqs, num_q_heads, num_kv_heads, head_dim, cache_dtype;
+  int32_t bt_stride;
+  int32_t max_seq_len;
+  int32_t partition_size;           // tokens per partition (partitioned mode)
+  int32_t max_num_partitions;
+  float scale;
+};
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                               int32_t bt_stride, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, int32_t num_reqs,
+                               int32_t max_query_len_hint, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key,
+                                    const void* value, int32_t num_tokens,
+                                    const int64_t* slot_mapping, int32_t num_kv_heads,
+                                    int32_t head_dim, hipStream_t stream);
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* cu_seq_lens, int32_t num_reqs,
+                            int32_t max_seq_len, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t elem_bytes, hipStream_t stream);
+
+hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
+                             hipStream_t stream);
+
+// Decode: partitioned == false writes args.out directly (one pass per
+// request and KV head); true writes the partials.
+hipError_t launch_decode(const DecodeArgs& args, bool partitioned, hipStream_t stream);
+
+hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits,
+                        const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
+                        int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                        int32_t max_num_partitions, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const float* k_scale;
+  const float* v_scale;
+  void* out;
+  int32_t num_reqs, num_q_heads, num_kv_heads, head_dim, cache_dtype;
+  int32_t bt_stride;
+  int32_t max_query_len, max_seq_len;
+  float scale;
+};
+
+// Rows of requests with q_len > 1 (the decode kernel takes the others).
+hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,108 @@
+"""Copies a host workload (paged_kv_cache_77_amd.workloads) to device tensors
+and calls the library on it.  Marshalling only: every step of the path runs
+in the HIP kernels of libpa."""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import (PA_CACHE_BF16, PA_CACHE_FP8_E4M3, make_layout, pa_compute_slot_mapping,
+               pa_decode, pa_decode_partitioned, pa_merge_partitions, pa_prefill_varlen,
+               pa_reshape_and_cache)
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on ``device``."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 numpy bit patterns (host copy)."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclasses.dataclass
+class DeviceWorkload:
+    w: object
+    layout: object
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    q: torch.Tensor
+    k_new: Optional[torch.Tensor]
+    v_new: Optional[torch.Tensor]
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    query_start_loc: torch.Tensor
+    k_scale: Optional[torch.Tensor]
+    v_scale: Optional[torch.Tensor]
+    max_seq_len: int
+    max_query_len: int
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+
+def to_device(w, device="cuda") -> DeviceWorkload:
+    fp8 = w.cache_dtype == "fp8"
+    if fp8:
+        kc = torch.from_numpy(w.k_pool).to(device)
+        vc = torch.from_numpy(w.v_pool).to(device)
+        ks = torch.tensor([w.k_scale], dtype=torch.float32, device=device)
+        vs = torch.tensor([w.v_scale], dtype=torch.float32, device=device)
+    else:
+        kc = bf16_tensor(w.k_pool, device)
+        vc = bf16_tensor(w.v_pool, device)
+        ks = vs = None
+    layout = make_layout(w.num_blocks, w.num_kv_heads, w.head_dim,
+                         PA_CACHE_FP8_E4M3 if fp8 else PA_CACHE_BF16)
+    return DeviceWorkload(
+        w=w, layout=layout, k_cache=kc, v_cache=vc, q=bf16_tensor(w.q, device),
+        k_new=None if w.k_new is None else bf16_tensor(w.k_new, device),
+        v_new=None if w.v_new is None else bf16_tensor(w.v_new, device),
+        block_table=torch.from_numpy(w.block_table).to(device),
+        seq_lens=torch.from_numpy(w.seq_lens).to(device),
+        query_start_loc=torch.from_numpy(w.query_start_loc).to(device),
+        k_scale=ks, v_scale=vs, max_seq_len=int(w.seq_lens.max()) if w.num_reqs else 0,
+        max_query_len=int(w.q_lens.max()) if w.num_reqs else 0)
+
+
+def partial_buffers(d: DeviceWorkload, partition_size: int):
+    """tmp_out, max_logits, exp_sums sized for the workload."""
+    R, H, D = d.w.num_reqs, d.w.num_q_heads, d.w.head_dim
+    pmax = max(1, -(-d.max_seq_len // partition_size))
+    dev = d.q.device
+    return (torch.empty((R, H, pmax, D), dtype=torch.float32, device=dev),
+            torch.empty((R, H, pmax), dtype=torch.float32, device=dev),
+            torch.empty((R, H, pmax), dtype=torch.float32, device=dev))
+
+
+def write_new_kv(d: DeviceWorkload, slot_mapping: torch.Tensor) -> None:
+    """Slot mapping then scatter of this step's new tokens."""
+    pa_compute_slot_mapping(slot_mapping, d.block_table, d.query_start_loc, d.seq_lens)
+    pa_reshape_and_cache(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new, slot_mapping)
+
+
+def run_decode(d: DeviceWorkload, out: torch.Tensor) -> None:
+    pa_decode(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+              d.max_seq_len, float(d.w.scale), d.k_scale, d.v_scale)
+
+
+def run_decode_partitioned(d: DeviceWorkload, out: torch.Tensor, partition_size: int,
+                           bufs=None):
+    tmp, ml, es = bufs if bufs is not None else partial_buffers(d, partition_size)
+    pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                          d.max_seq_len, float(d.w.scale), partition_size, tmp, ml, es,
+                          d.k_scale, d.v_scale)
+    pa_merge_partitions(out, tmp, ml, es, d.seq_lens, partition_size)
+    return tmp, ml, es
+
+
+def run_prefill(d: DeviceWorkload, out: torch.Tensor) -> None:
+    pa_prefill_varlen(d.layout, out, d.q, d.k_cache, d.v_cache, d.query_start_loc,
+                      d.seq_lens, d.block_table, d.max_query_len, d.max_seq_len,
+                      float(d.w.scale), d.k_scale, d.v_scale)
