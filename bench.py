@@ -1,0 +1,249 @@
+#!/usr/bin/env python
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one pass of the hot path over one batch: slot mapping of the
+step's new tokens, their scatter into the paged cache (reshape_and_cache),
+then paged decode attention over every request (split-KV + merge, or a
+single pass), for the batched-decode workload (64 requests, contexts
+uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
+16-token blocks, one layer).  Other workloads are selected with --config.
+
+Prints ONE JSON line.  value = algorithmic decode bytes (K and V read once
+per KV head, plus Q, O, block-table entries and seq_lens) per second of
+whole step; the roofline object reports the dominant kernel alone, timed
+with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+DESCR = {
+    1: "tiny decode: 4 requests, contexts 1/17/33/100, 4 q / 2 KV heads, head_dim 64, bf16",
+    2: "batched decode: 64 requests, contexts U[512,4096], 32 q / 8 KV heads, head_dim 128, "
+       "bf16, block 16, one layer; 64 new tokens scattered per step",
+    3: "long-context split-KV decode: 8 requests x 32768 tokens, 32 q / 8 KV heads, "
+       "head_dim 128, bf16, 512-token partitions + merge",
+    4: "mixed chunked-prefill batch: 128 decode rows (contexts U[1024,8192]) + one "
+       "2048-token chunk on a 6144-token prefix, 32 q / 8 KV heads, head_dim 128, bf16",
+    5: "shared-prefix fp8 decode: 256 requests sharing a 4096-token prefix + tails "
+       "U[64,1024], 28 q / 4 KV heads, head_dim 128, fp8 e4m3 K/V",
+}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_device.h", "pa_prefill.hip", "pa_cache_ops.hip"):
+        p = os.path.join(ROOT, "paged_kv_cache_77_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(w) -> dict:
+    """Algorithmic bytes of decode attention over workload w."""
+    import numpy as np
+    eb = 1 if w.cache_dtype == "fp8" else 2
+    ctx = w.seq_lens.astype(np.int64)
+    kv = int(ctx.sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+    qo = 2 * w.num_reqs * w.num_q_heads * w.head_dim * 2
+    bt = 4 * int(((ctx + 15) // 16).sum())
+    return {"kv": kv, "q_o": qo, "table": bt + 4 * w.num_reqs, "tokens": int(ctx.sum()),
+            "total": kv + qo + bt + 4 * w.num_reqs}
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the
+    current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands, on the host cores, over whole passes of the
+    workload's decode (the sample: complete passes until ~budget_s)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    nbytes = decode_bytes(w)
+    t0 = time.perf_counter()
+    reqs_done = 0
+    while True:
+        for r in range(w.num_reqs):
+            oracle.decode(w, requests=[r])
+            reqs_done += 1
+            if time.perf_counter() - t0 > 30.0:
+                break
+        el = time.perf_counter() - t0
+        if el >= budget_s or el > 30.0:
+            break
+    dt = time.perf_counter() - t0
+    frac = reqs_done / w.num_reqs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(nbytes["total"] * frac / dt / 1e9, 4), "unit": "GB/s",
+            "tokens_per_s": round(nbytes["tokens"] * frac / dt, 1),
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{reqs_done} request decodes ({frac:.2f} passes over all "
+                      f"{w.num_reqs} requests, all heads) in {dt:.1f} s, fp64 numpy"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--path", choices=["split", "single"], default="split")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="split-KV partition size in tokens (0 = the workload's default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return 0
+
+    import paged_kv_cache_77_amd as pa
+    from paged_kv_cache_77_amd import device as dv
+    from paged_kv_cache_77_amd import workloads as wl
+
+    pa.lib()
+    w = wl.config_workload(args.config, poison=False)
+    d = dv.to_device(w, "cuda")
+    nbytes = decode_bytes(w)
+    P = args.partition_size or (w.partition_size if args.config == 3 else 256)
+    is_prefill = args.config == 4
+    T = w.num_tokens
+    sm = torch.empty((max(T, 1),), dtype=torch.int64, device="cuda")
+    if is_prefill:
+        out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    else:
+        out = torch.empty((w.num_reqs, w.num_q_heads, w.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+    bufs = dv.partial_buffers(d, P) if not is_prefill else None
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(timed: bool):
+        if w.writes_new_kv:
+            dv.write_new_kv(d, sm[:T])
+        e0 = e1 = None
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        if is_prefill:
+            dv.run_prefill(d, out)
+        elif args.path == "single":
+            dv.run_decode(d, out)
+        else:
+            tmp, ml, es = bufs
+            pa.pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
+                                     d.seq_lens, d.max_seq_len, float(w.scale), P, tmp, ml,
+                                     es, d.k_scale, d.v_scale)
+            if timed:
+                e1.record(stream)
+            pa.pa_merge_partitions(out, tmp, ml, es, d.seq_lens, P)
+        if timed:
+            if is_prefill or args.path == "single":
+                e1.record(stream)
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    if is_prefill:
+        kernel = "pa_prefill_varlen (decode rows + prefill rows)"
+        kbytes = nbytes["total"]
+    elif args.path == "single":
+        kernel = "decode_kernel (single pass)"
+        kbytes = nbytes["total"]
+    else:
+        kernel = f"decode_kernel (split-KV, P={P})"
+        nparts = int(((w.seq_lens + P - 1) // P).sum())
+        part_bytes = nparts * w.num_q_heads * (w.head_dim + 2) * 4
+        kbytes = nbytes["total"] - nbytes["q_o"] // 2 + part_bytes
+    achieved = kbytes / (kern_ms * 1e-3) / 1e9
+    key = f"config{args.config}_{args.path}"
+    tr = traffic_for(key)
+    value = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode attn HBM GB/s (% of MI355X peak) + attended KV tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if w.cache_dtype == "fp8" else "bf16",
+        "data": "synthetic (seeded PCG64 N(0,1), random block permutation)",
+        "config": {"workload": DESCR[args.config], "requests": w.num_reqs,
+                   "kv_tokens": nbytes["tokens"], "path": args.path if not is_prefill else
+                   "varlen", "partition_size": P if args.path == "split" else None,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "kv_tokens_per_s": round(nbytes["tokens"] / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": nbytes["total"],
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": tr, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes_per_launch": kbytes},
+        "kernel_sha": kernel_source_sha(),
+        "inputs_sha256": w.digest(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

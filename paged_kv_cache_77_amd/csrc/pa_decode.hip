@@ -40,7 +40,7 @@ constexpr float kTau = 8.0f;
 template <int D, int GC, bool FP8>
 struct DecodeShape {
   static constexpr int EB = FP8 ? 1 : 2;                    // bytes per element
-  static constexpr int LPR = (FP8 || GC > 4) ? 8 : 4;       // K lanes per row
+  static constexpr int LPR = 8;                             // K lanes per row
   static constexpr int RK = LPR / 4;                        // K rows per lane
   static constexpr int KE = D / LPR;                        // K elements per lane-row
   static constexpr int KBYTES = KE * EB;                    // K bytes per lane-row
@@ -76,9 +76,12 @@ __device__ __forceinline__ Words<N> load_words(const uint8_t* p) {
   return r;
 }
 
+constexpr int kBtChunk = 1024;   // block-table entries staged in LDS at a time
+
 template <int D, int GC, bool FP8, int WAVES>
 struct DecodeSmem {
   using S = DecodeShape<D, GC, FP8>;
+  int32_t bt[kBtChunk];
   float p[WAVES][2][kBlock][S::GCP];
   float m[WAVES][8];
   float mt[WAVES][8];
@@ -161,11 +164,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
 
-  // ---- block range of this wave
+  // ---- block range of the work-group
   const int first_block = t_begin / kBlock;
   const int last_block = (t_end - 1) / kBlock;
-  const int n_blocks = last_block - first_block + 1;
-  const int n_my = n_blocks > w ? (n_blocks - w + WAVES - 1) / WAVES : 0;
   const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
@@ -186,13 +187,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
     Words<VW> v[4];
   };
 
-  int bt_vec = 0;                // block ids of this wave's next 64 blocks
-  auto load_bt = [&](int it0) {
-    const int it = it0 + lane;
-    bt_vec = it < n_my ? bt_row[first_block + w + it * WAVES] : 0;
-  };
-  auto load_tile = [&](Tile& t, int it) {
-    const int32_t phys = __builtin_amdgcn_readlane(bt_vec, it & 63);
+  auto load_tile = [&](Tile& t, int32_t phys) {
     const int64_t off = tile_offset(phys, g, Hkv, D) * EB;
     const uint8_t* kt = kbase + off;
     const uint8_t* vt = vbase + off;
@@ -207,9 +202,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
       t.v[i] = load_words<VW>(vt + ((vrg + 4 * i) * D + vcol) * EB);
   };
 
-  auto compute = [&](Tile& t, int it, int buf) {
-    const int b = first_block + w + it * WAVES;
-    const int tok0 = b * kBlock;
+  auto compute = [&](Tile& t, int tok0, int buf) {
     // -- scores of the chunk's heads for this lane's K rows
     float s[RK][GC];
 #pragma unroll
@@ -331,22 +324,34 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
     }
   };
 
-  if (n_my > 0) {
-    Tile ta, tb;
-    load_bt(0);
-    load_tile(ta, 0);
-    for (int it = 0; it < n_my; it += 2) {
-      if (it + 1 < n_my) {
-        if (((it + 1) & 63) == 0) load_bt(it + 1);
-        load_tile(tb, it + 1);
+  // Walk the range in chunks of kBtChunk blocks whose block-table entries are
+  // staged in LDS.  Within a chunk each wave double-buffers its tiles; the
+  // prefetch is unconditional (the index is clamped to the wave's last block,
+  // a repeat read that hits in L2) so every iteration has the same loads in
+  // flight and the compiler's wait counts stay exact.
+  for (int cb = first_block; cb <= last_block; cb += kBtChunk) {
+    const int nb = min(last_block + 1 - cb, kBtChunk);
+    __syncthreads();
+    for (int i = tid; i < nb; i += WAVES * kWave) sm.bt[i] = bt_row[cb + i];
+    __syncthreads();
+    const int n = nb > w ? (nb - w + WAVES - 1) / WAVES : 0;   // this wave's blocks
+    if (n > 0) {
+      auto phys_of = [&](int it) {
+        return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * WAVES]);
+      };
+      auto tok0_of = [&](int it) { return (cb + w + it * WAVES) * kBlock; };
+      Tile ta, tb;
+      load_tile(ta, phys_of(0));
+      int32_t pn = phys_of(1);
+      for (int it = 0; it < n; it += 2) {
+        load_tile(tb, pn);
+        pn = phys_of(it + 2);
+        compute(ta, tok0_of(it), 0);
+        if (it + 1 >= n) break;
+        load_tile(ta, pn);
+        pn = phys_of(it + 3);
+        compute(tb, tok0_of(it + 1), 1);
       }
-      compute(ta, it, 0);
-      if (it + 1 >= n_my) break;
-      if (it + 2 < n_my) {
-        if (((it + 2) & 63) == 0) load_bt(it + 2);
-        load_tile(ta, it + 2);
-      }
-      compute(tb, it + 1, 1);
     }
   }
 
