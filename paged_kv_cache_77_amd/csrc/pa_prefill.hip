@@ -1,9 +1,307 @@
-// Varlen chunked prefill (rows of requests with q_len > 1): not built yet.
+// Varlen chunked prefill over the paged cache, MFMA tiles for gfx950.
+//
+// What is computed ("第11章 分块预填充与混合批处理" §11.6; "vLLM 深度解析（二）：
+// PagedAttention 核心机制" §2 and §5.2): request r owns query rows
+// query_start_loc[r] .. query_start_loc[r+1]-1; row i sits at position
+// seq_len - q_len + i and attends keys 0..position (causal), K/V read through
+// block_table[r][t / 16].  Tiles of keys are folded in with the running
+// (m, l, A) state, so S and P never reach HBM (§2.1/§2.2 of the second page).
+// Rows of requests with q_len <= 1 are left to the decode kernel.
+//
+// Work-group: (request, query head, 128-query tile); 4 waves x 32 queries.
+// Per 64-key tile (4 cache blocks):
+//   S^T[64 keys x 32 queries] = K . Q^T   (v_mfma_f32_32x32x16_bf16; keys on
+//       the M side so each lane owns one query column: the softmax row
+//       reductions are in-lane plus one swap with lane^32)
+//   O^T[d x 32 queries] += V^T . P^T      (P^T comes straight from the S^T
+//       accumulators: the MFMA contraction order over keys is permuted to the
+//       order the accumulators hold them, and V^T is stored in LDS in that
+//       order)
+// K is staged row-major with a 16-byte-chunk XOR swizzle, V transposed
+// (d-major) with the key permutation and a swizzle; both double-buffered.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128;        // queries per work-group
+constexpr int kBN = 64;         // keys per tile
+constexpr int kWaves = 4;
+constexpr int kQW = 32;         // queries per wave
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Slot of key k (0..63) inside the V^T rows: within each group of 16 keys,
+// bits 2 and 3 are swapped (the order the S^T accumulators hold keys in).
+__device__ __forceinline__ int vt_slot(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int D>
+struct PrefillSmem {
+  uint4 k[2][kBN * D / 8];        // [key][16-byte chunk ^ (key & 15)]
+  uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ (d & 7)]
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, int tiles_x) {
+  constexpr int CH = D / 8;               // 16-byte chunks per bf16 row
+  constexpr int KSTEPS = D / 16;          // MFMA k-steps over d
+  constexpr int DBLK = D / 32;            // 32-row d blocks of O^T
+  __shared__ PrefillSmem<D> sm;
+
+  // ---- which (request, head, query tile)
+  const int r = blockIdx.y;
+  const int Hq = a.num_q_heads;
+  int hid = blockIdx.x % Hq;
+  const int tile = blockIdx.x / Hq;
+  if (Hq % 8 == 0) hid = (hid % 8) * (Hq / 8) + hid / 8;   // a KV group stays on one XCD
+  const int h = hid;
+  (void)tiles_x;
+  const int qlo = a.query_start_loc[r];
+  const int q_len = a.query_start_loc[r + 1] - qlo;
+  if (q_len <= 1) return;                                   // decode path
+  const int i0 = tile * kBM;
+  if (i0 >= q_len) return;
+  const int seq_len = a.seq_lens[r];
+  const int pos0 = seq_len - q_len;                         // position of query 0
+  const int G = Hq / a.num_kv_heads;
+  const int g = h / G;
+  const int Hkv = a.num_kv_heads;
+
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  const int lq = lane % 32, lh = lane / 32;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query lq, d = 16k + 8lh .. +8
+  const int qi = i0 + w * kQW + lq;                         // query index in request
+  const bool q_ok = qi < q_len;
+  uint4 qf[KSTEPS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(qlo + (q_ok ? qi : 0)) * Hq + h) * D;
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * k + 8 * lh);
+      qf[k] = q_ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int p_q = pos0 + qi;                                // this lane's query position
+  const int wave_pmin = pos0 + i0 + w * kQW;                // first query position of the wave
+  const int wave_pmax = pos0 + min(i0 + (w + 1) * kQW, q_len) - 1;
+  const int kend = pos0 + min(i0 + kBM, q_len);             // keys the work-group needs
+  const int n_tiles = (kend + kBN - 1) / kBN;
+
+  float qk_scale = a.scale * kLog2e;
+  if constexpr (FP8) qk_scale *= *a.k_scale;
+
+  const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
+  constexpr int EB = FP8 ? 1 : 2;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+
+  // ---- global -> registers -> LDS staging of one 64-key tile.
+  // K: thread handles chunks u = tid + 256 i (key u / CH, chunk u % CH): rows
+  // stream contiguously.  V: key = u % 64 (lane-fast), chunk u / 64, so the
+  // transposed 2-byte LDS stores of a wave land on consecutive slots.
+  constexpr int NCH = kBN * CH / (kWaves * 64);             // chunks per thread per tensor
+  uint4 kreg[NCH], vreg[NCH];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      {
+        const int u = tid + kWaves * 64 * i;
+        const int key = u / CH, c = u % CH;
+        const int t = kt * kBN + key;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < seq_len) {
+          const int32_t phys = bt_row[t / kBlock];
+          const uint8_t* p = kbase + (tile_offset(phys, g, Hkv, D) + (int64_t)(t % kBlock) * D) * EB;
+          if constexpr (FP8) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(p + c * 8);
+            const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
+            v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+          } else {
+            v = *reinterpret_cast<const uint4*>(p + c * 16);
+          }
+        }
+        kreg[i] = v;
+      }
+      {
+        const int u = tid + kWaves * 64 * i;
+        const int key = u % kBN, c = u / kBN;
+        const int t = kt * kBN + key;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < seq_len) {                                    // past the context: zero
+          const int32_t phys = bt_row[t / kBlock];
+          const uint8_t* p = vbase + (tile_offset(phys, g, Hkv, D) + (int64_t)(t % kBlock) * D) * EB;
+          if constexpr (FP8) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(p + c * 8);
+            const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
+            v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+          } else {
+            v = *reinterpret_cast<const uint4*>(p + c * 16);
+          }
+        }
+        vreg[i] = v;
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+    uint16_t* vt16 = reinterpret_cast<uint16_t*>(&sm.vt[buf][0]);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      {
+        const int u = tid + kWaves * 64 * i;
+        const int key = u / CH, c = u % CH;
+        sm.k[buf][key * CH + (c ^ (key & (CH - 1)))] = kreg[i];
+      }
+      {
+        const int u = tid + kWaves * 64 * i;
+        const int key = u % kBN, c = u / kBN;
+        const int slot = vt_slot(key);
+        const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = c * 8 + e;
+          const int chunk = (slot / 8) ^ (d & 7);
+          vt16[d * kBN + chunk * 8 + (slot % 8)] =
+              (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
+        }
+      }
+    }
+  };
+
+  // ---- running state of this lane's query (keys split between lane halves)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t oacc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[b][v] = 0.f;
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < n_tiles;
+    if (more) fetch(kt + 1);
+    const int k0 = kt * kBN;
+    if (k0 <= wave_pmax) {                      // some key of the tile is visible to the wave
+      // -- S^T = K Q^T for the two 32-key halves of the tile
+      f32x16_t s[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[b][v] = 0.f;
+        const int key = 32 * b + lq;
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) {
+          const int c = 2 * k + lh;
+          const uint4 kf = sm.k[buf][key * CH + (c ^ (key & (CH - 1)))];
+          s[b] = mfma32(kf, qf[k], s[b]);
+        }
+      }
+      // -- scale, causal mask (select), tile max
+      const bool diag = k0 + kBN - 1 > wave_pmin;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = s[b][v] * qk_scale;
+          if (diag) {
+            const int t = k0 + 32 * b + 8 * (v / 4) + 4 * lh + (v % 4);
+            x = (t <= p_q) ? x : -INFINITY;
+          }
+          s[b][v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, xor_lanes(tmax, 32));
+      // -- lazy rescale: move the max only when it grows by more than 2^8
+      if (tmax > m_run + 8.0f) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - tmax);
+        m_run = tmax;
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[b][v] *= alpha;
+      }
+      // -- P^T as bf16 B operands: k-step (b, s') takes accumulator rows 8s'..8s'+7
+      uint4 pf[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[b][8 * sp + e];
+            p[e] = (x == -INFINITY) ? 0.f : fast_exp2(x - m_run);
+            l_run += p[e];
+          }
+          pf[2 * b + sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+        }
+      // -- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const int d = 32 * db + lq;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int chunk = (2 * ks + lh) ^ (d & 7);
+          const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
+          oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+        }
+      }
+    }
+    if (more) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finalize: l over both lane halves, O = A / l, write bf16 rows
+  const float l_tot = l_run + xor_lanes(l_run, 32);
+  if (q_ok) {
+    float inv = 1.f / l_tot;
+    if constexpr (FP8) inv *= *a.v_scale;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(qlo + qi) * Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * db + 8 * i + 4 * lh;
+        const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[db][4 * i + 0] * inv) |
+                            ((uint32_t)f32_to_bf16(oacc[db][4 * i + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[db][4 * i + 2] * inv) |
+                            ((uint32_t)f32_to_bf16(oacc[db][4 * i + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+      }
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  if (a.num_reqs == 0 || a.max_query_len <= 1) return hipSuccess;
+  const int tiles = (a.max_query_len + kBM - 1) / kBM;
+  dim3 grid(tiles * a.num_q_heads, a.num_reqs);
+  const bool fp8 = a.cache_dtype != 0;
+  if (a.head_dim == 64) {
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+    else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+  } else {
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+    else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace pa

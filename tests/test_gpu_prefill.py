@@ -1,0 +1,122 @@
+"""GPU parity of varlen chunked prefill (MFMA tiles) and its decode rows."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_77_amd import workloads as wl
+from paged_kv_cache_77_amd import device as dv
+from tests.parity import check_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _run(w, write=True):
+    d = dv.to_device(w)
+    kp, vp = w.k_pool, w.v_pool
+    if write and w.writes_new_kv:
+        sm = torch.empty((w.num_tokens,), dtype=torch.int64, device="cuda")
+        dv.write_new_kv(d, sm)
+        ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+        kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
+    out = torch.full((w.num_tokens, w.num_q_heads, w.head_dim), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    dv.run_prefill(d, out)
+    torch.cuda.synchronize()
+    return dv.bits_of(out), kp, vp
+
+
+MIX = dict(seq_lens=[1, 40, 300, 129, 700, 64, 2, 5000],
+           q_lens=[1, 17, 300, 2, 129, 0, 2, 1000])
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (4, 2, 64), (28, 4, 128), (8, 8, 128),
+                                      (16, 1, 64)])
+def test_prefill_mixed_batch(hq, hkv, d):
+    _announce(f"prefill mix hq={hq} hkv={hkv} d={d}")
+    w = wl.make_workload(name="t", num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                         seed=41 + hq + d, bt_extra_cols=2, **MIX)
+    got, kp, vp = _run(w)
+    ref = oracle.prefill_varlen(w, k_pool=kp, v_pool=vp)
+    check_bf16(got, ref, f"prefill {hq}/{hkv}/{d}")
+
+
+def test_prefill_fp8_cache():
+    _announce("prefill fp8 cache")
+    w = wl.make_workload(name="t", num_q_heads=28, num_kv_heads=4, head_dim=128, seed=47,
+                         cache_dtype="fp8", writes_new_kv=False, **MIX)
+    got, _, _ = _run(w)
+    check_bf16(got, oracle.prefill_varlen(w), "prefill fp8")
+
+
+def test_prefill_whole_prompt_and_orders():
+    """q_len == seq_len (textbook causal) and the prefill row placed first or last."""
+    _announce("prefill whole prompt / order")
+    for order in ([0, 1, 2], [2, 0, 1]):
+        sl = np.array([200, 1, 77])[order]
+        ql = np.array([200, 1, 77])[order]
+        w = wl.make_workload(name="t", seq_lens=sl, q_lens=ql, num_q_heads=8, num_kv_heads=2,
+                             head_dim=128, seed=48)
+        got, kp, vp = _run(w)
+        check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), f"order {order}")
+
+
+@pytest.mark.parametrize("prefill_first,share", [(False, 0), (True, 0), (False, 16)])
+def test_config4_scaled(prefill_first, share):
+    """The mixed chunked-prefill configuration at 1/8 scale: 16 decode rows and
+    a 256-token chunk on a 768-token prefix (optionally 16 decode rows share
+    the chunk's first cached blocks)."""
+    _announce(f"config 4 / 8, prefill_first={prefill_first}, share={share}")
+    w = wl.config_workload(4, scale_down=8, prefill_first=prefill_first,
+                           share_prefix_rows=share)
+    got, kp, vp = _run(w)
+    check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "config 4 / 8")
+
+
+def test_chunked_equals_whole():
+    """One 512-token chunk vs two 256-token chunks (the first written to the
+    cache, the second resuming on it): same rows within tolerance."""
+    _announce("chunk composition")
+    base = wl.make_workload(name="t", seq_lens=[1536], q_lens=[512], num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, seed=49)
+    got_whole, kp, vp = _run(base)
+    ref = oracle.prefill_varlen(base, k_pool=kp, v_pool=vp)
+    check_bf16(got_whole, ref, "whole chunk")
+    # second half of the chunk as its own step on the same cache contents
+    d = dv.to_device(dataclasses.replace(base, k_pool=kp, v_pool=vp))
+    half = dataclasses.replace(base, q_lens=np.array([256], np.int32),
+                               query_start_loc=np.array([0, 256], np.int32), q=base.q[256:],
+                               k_new=None, v_new=None, writes_new_kv=False, k_pool=kp, v_pool=vp)
+    d2 = dv.to_device(half)
+    out = torch.empty((256, 8, 128), dtype=torch.bfloat16, device="cuda")
+    dv.run_prefill(d2, out)
+    first = dataclasses.replace(half, seq_lens=np.array([1280], np.int32), q=base.q[:256])
+    d1 = dv.to_device(first)
+    out1 = torch.empty((256, 8, 128), dtype=torch.bfloat16, device="cuda")
+    dv.run_prefill(d1, out1)
+    torch.cuda.synchronize()
+    del d
+    halves = np.concatenate([dv.bits_of(out1), dv.bits_of(out)])
+    check_bf16(halves, ref, "two chunks")
+
+
+def test_config4_full_size_sampled():
+    """Full mixed batch (128 decode rows + 2048-token chunk on 6144 cached
+    tokens) in the benchmark's launch configuration; the oracle computes a
+    sample of rows."""
+    _announce("config 4 full size")
+    w = wl.config_workload(4)
+    got, kp, vp = _run(w)
+    rng = np.random.default_rng(4)
+    pre = int(w.query_start_loc[-2])            # the prefill row's first token
+    toks = sorted(set(rng.integers(pre, w.num_tokens, size=24).tolist())
+                  | {pre, pre + 1, w.num_tokens - 1} | set(rng.integers(0, pre, 8).tolist()))
+    rows = [(t, h) for t in toks for h in range(w.num_q_heads)]
+    ref = oracle.prefill_varlen(w, rows=rows, k_pool=kp, v_pool=vp)
+    check_bf16(got[toks], ref[toks], "config 4 sampled rows")
