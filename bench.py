@@ -110,7 +110,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", choices=["split", "single"], default="split")
+    ap.add_argument("--path", choices=["auto", "split", "single"], default="auto",
+                    help="decode path; auto = split-KV for the long-context workload, "
+                         "single pass otherwise (measured faster for these batches)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition size in tokens (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,7 +148,9 @@ def main() -> int:
     w = wl.config_workload(args.config, poison=False)
     d = dv.to_device(w, "cuda")
     nbytes = decode_bytes(w)
-    P = args.partition_size or (w.partition_size if args.config == 3 else 256)
+    if args.path == "auto":
+        args.path = "split" if args.config == 3 else "single"
+    P = args.partition_size or (w.partition_size if args.config == 3 else 1024)
     is_prefill = args.config == 4
     T = w.num_tokens
     sm = torch.empty((max(T, 1),), dtype=torch.int64, device="cuda")
@@ -195,6 +199,37 @@ def main() -> int:
     ms_step = dt * 1e3 / args.steps
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
+    prefill = None
+    if is_prefill:
+        # the prefill row alone (q_len > 1), timed with events around its launch
+        r = int(np.argmax(w.q_lens))
+        lo, hi = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
+        qsl1 = torch.tensor([0, hi - lo], dtype=torch.int32, device="cuda")
+        args1 = (d.layout, out[lo:hi], d.q[lo:hi], d.k_cache, d.v_cache, qsl1,
+                 d.seq_lens[r:r + 1], d.block_table[r:r + 1], hi - lo, int(w.seq_lens[r]),
+                 float(w.scale), d.k_scale, d.v_scale)
+        for _ in range(3):
+            pa.pa_prefill_varlen(*args1)
+        pe = []
+        for _ in range(max(5, args.steps // 2)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_prefill_varlen(*args1)
+            e1.record(stream)
+            pe.append((e0, e1))
+        torch.cuda.synchronize()
+        pms = sum(a.elapsed_time(b) for a, b in pe) / len(pe)
+        n, ql = int(w.seq_lens[r]), hi - lo
+        pairs = ql * (n - ql) + ql * (ql + 1) // 2
+        flops = 4 * w.head_dim * w.num_q_heads * pairs
+        prefill = {"bound": "mfma", "kernel": "prefill_kernel (MFMA 32x32x16 bf16)",
+                   "achieved": round(flops / (pms * 1e-3) / 1e12, 2),
+                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(flops / (pms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "traffic": traffic_for("config4_prefill"), "kernel_ms": round(pms, 5),
+                   "algorithmic_flops_per_launch": flops, "visible_pairs_per_head": pairs}
+
     if is_prefill:
         kernel = "pa_prefill_varlen (decode rows + prefill rows)"
         kbytes = nbytes["total"]
@@ -225,8 +260,8 @@ def main() -> int:
         "data": "synthetic (seeded PCG64 N(0,1), random block permutation)",
         "config": {"workload": DESCR[args.config], "requests": w.num_reqs,
                    "kv_tokens": nbytes["tokens"], "path": args.path if not is_prefill else
-                   "varlen", "partition_size": P if args.path == "split" else None,
-                   "parallelism": "none (1 GPU)"},
+                   "varlen", "partition_size": P if (args.path == "split" and not is_prefill)
+                   else None, "parallelism": "none (1 GPU)"},
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "kv_tokens_per_s": round(nbytes["tokens"] / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nbytes["total"],
@@ -238,6 +273,8 @@ def main() -> int:
         "kernel_sha": kernel_source_sha(),
         "inputs_sha256": w.digest(),
     }
+    if prefill is not None:
+        res["prefill_roofline"] = prefill
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
         res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)

@@ -23,7 +23,8 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpa.so")
+# PA_LIBRARY may point at another build of the same sources (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(HERE, "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1

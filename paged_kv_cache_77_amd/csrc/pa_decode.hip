@@ -37,6 +37,20 @@ namespace pa {
 
 constexpr float kTau = 8.0f;
 
+// Waves per work-group for the single-pass and split-KV launches (measured on
+// MI355X: the single pass gains from spreading a long context over more
+// waves, split-KV partitions from more work-groups), and the prefetch depth
+// (tiles in flight while one is computed; 2 measured no better than 1).
+#ifndef PA_DECODE_WAVES_SINGLE
+#define PA_DECODE_WAVES_SINGLE 8
+#endif
+#ifndef PA_DECODE_WAVES_SPLIT
+#define PA_DECODE_WAVES_SPLIT 4
+#endif
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 1
+#endif
+
 template <int D, int GC, bool FP8>
 struct DecodeShape {
   static constexpr int EB = FP8 ? 1 : 2;                    // bytes per element
@@ -91,7 +105,7 @@ struct DecodeSmem {
 
 // PART: false -> write the final bf16 output; true -> write the partition
 // partials.  QSL: q/out rows come from query_start_loc (varlen decode rows).
-template <int D, int GC, bool FP8, int WAVES, bool PART>
+template <int D, int GC, bool FP8, int WAVES, bool PART, int PD>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_chunks) {
   using S = DecodeShape<D, GC, FP8>;
   constexpr int EB = S::EB, LPR = S::LPR, RK = S::RK, KCH = S::KCH, KW = S::KW,
@@ -340,17 +354,37 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
         return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * WAVES]);
       };
       auto tok0_of = [&](int it) { return (cb + w + it * WAVES) * kBlock; };
-      Tile ta, tb;
-      load_tile(ta, phys_of(0));
-      int32_t pn = phys_of(1);
-      for (int it = 0; it < n; it += 2) {
-        load_tile(tb, pn);
-        pn = phys_of(it + 2);
-        compute(ta, tok0_of(it), 0);
-        if (it + 1 >= n) break;
-        load_tile(ta, pn);
-        pn = phys_of(it + 3);
-        compute(tb, tok0_of(it + 1), 1);
+      if constexpr (PD == 1) {
+        Tile ta, tb;
+        load_tile(ta, phys_of(0));
+        int32_t pn = phys_of(1);
+        for (int it = 0; it < n; it += 2) {
+          load_tile(tb, pn);
+          pn = phys_of(it + 2);
+          compute(ta, tok0_of(it), 0);
+          if (it + 1 >= n) break;
+          load_tile(ta, pn);
+          pn = phys_of(it + 3);
+          compute(tb, tok0_of(it + 1), 1);
+        }
+      } else {                                  // two tiles in flight while computing
+        Tile t0, t1, t2;
+        load_tile(t0, phys_of(0));
+        load_tile(t1, phys_of(1));
+        int32_t pn = phys_of(2);
+        for (int it = 0; it < n; it += 3) {
+          load_tile(t2, pn);
+          pn = phys_of(it + 3);
+          compute(t0, tok0_of(it), it & 1);
+          if (it + 1 >= n) break;
+          load_tile(t0, pn);
+          pn = phys_of(it + 4);
+          compute(t1, tok0_of(it + 1), (it + 1) & 1);
+          if (it + 2 >= n) break;
+          load_tile(t1, pn);
+          pn = phys_of(it + 5);
+          compute(t2, tok0_of(it + 2), it & 1);
+        }
       }
     }
   }
@@ -464,16 +498,18 @@ template <int D, int GC, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStream_t st) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int n_chunks = (G + GC - 1) / GC;
-  constexpr int WAVES = 4;
+  constexpr int PD = PA_DECODE_PREFETCH;
   if (partitioned) {
+    constexpr int WAVES = PA_DECODE_WAVES_SPLIT;
     const int nparts = (a.max_seq_len + a.partition_size - 1) / a.partition_size;
     if (nparts == 0) return hipSuccess;
     dim3 grid(nparts, a.num_kv_heads * n_chunks, a.num_reqs);
-    hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, true>), grid, dim3(WAVES * 64), 0, st,
+    hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, true, PD>), grid, dim3(WAVES * 64), 0, st,
                        a, n_chunks);
   } else {
+    constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
     dim3 grid(1, a.num_kv_heads * n_chunks, a.num_reqs);
-    hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false>), grid, dim3(WAVES * 64), 0, st,
+    hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0, st,
                        a, n_chunks);
   }
   return hipGetLastError();
