@@ -462,33 +462,85 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
 }
 
 // ---------------------------------------------------------------------------
-// merge of partition partials: one wave per (request, query head)
+// merge of partition partials ("vLLM 深度解析（二）：PagedAttention 核心机制"
+// §3.2.9): one 256-thread work-group per (request, query head).  The
+// partition weights l_j e^(m_j - m) go to LDS first; then groups of D/4
+// threads each read one partition row with 16-byte loads, so 256/(D/4)
+// partitions are in flight per step, and the groups are summed in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxParts = 2048;    // partitions held in LDS per pass
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ tmp_out,
     const float* __restrict__ max_logits, const float* __restrict__ exp_sums,
     const int32_t* __restrict__ seq_lens, int32_t num_q_heads, int32_t partition_size,
     int32_t max_num_partitions) {
-  constexpr int E = D / 64;
-  const int r = blockIdx.y, h = blockIdx.x, lane = threadIdx.x;
+  constexpr int TPR = D / 4;                    // threads per partition row
+  constexpr int PG = kMergeThreads / TPR;       // partition rows per step
+  __shared__ float wgt[kMergeMaxParts];
+  __shared__ float red[kMergeThreads];
+  __shared__ f32x4_t part[PG][TPR];
+  const int r = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   const int n = (seq_lens[r] + partition_size - 1) / partition_size;
   const int64_t base = ((int64_t)r * num_q_heads + h) * max_num_partitions;
+  const int pg = tid / TPR, c = tid % TPR;
+
+  // global max of the partition maxima
   float M = -INFINITY;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, max_logits[base + p]);
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, xor_lanes(M, s));
-  float L = 0.f, O[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) O[e] = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float wgt = exp_sums[base + p] * fast_exp2((max_logits[base + p] - M) * kLog2e);
-    L += wgt;
-#pragma unroll
-    for (int e = 0; e < E; ++e) O[e] = fmaf(wgt, tmp_out[(base + p) * D + lane * E + e], O[e]);
+  for (int p = tid; p < n; p += kMergeThreads) M = fmaxf(M, max_logits[base + p]);
+  red[tid] = M;
+  __syncthreads();
+  for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
   }
-  uint16_t* o = out + ((int64_t)r * num_q_heads + h) * D + lane * E;
+  M = red[0];
+  __syncthreads();
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int p0 = 0; p0 < n; p0 += kMergeMaxParts) {
+    const int np = min(n - p0, kMergeMaxParts);
+    float lsum = 0.f;
+    for (int p = tid; p < np; p += kMergeThreads) {
+      const float w = exp_sums[base + p0 + p] * fast_exp2((max_logits[base + p0 + p] - M) * kLog2e);
+      wgt[p] = w;
+      lsum += w;
+    }
+    red[tid] = lsum;
+    __syncthreads();
+    for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    L += red[0];
+    const f32x4_t* rows = reinterpret_cast<const f32x4_t*>(tmp_out + (base + p0) * D);
+#pragma unroll 4
+    for (int p = pg; p < np; p += PG) {
+      const f32x4_t v = rows[(int64_t)p * TPR + c];
+      const float w = wgt[p];
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
+    __syncthreads();
+  }
+  part[pg][c] = acc;
+  __syncthreads();
+  if (pg == 0) {
+    f32x4_t sum = part[0][c];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = n ? f32_to_bf16(O[e] / L) : (uint16_t)0;
+    for (int g = 1; g < PG; ++g) {
+      sum.x += part[g][c].x; sum.y += part[g][c].y;
+      sum.z += part[g][c].z; sum.w += part[g][c].w;
+    }
+    const float inv = n ? 1.f / L : 0.f;
+    const uint32_t w0 = (uint32_t)f32_to_bf16(sum.x * inv) | ((uint32_t)f32_to_bf16(sum.y * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(sum.z * inv) | ((uint32_t)f32_to_bf16(sum.w * inv) << 16);
+    *reinterpret_cast<uint2*>(out + ((int64_t)r * num_q_heads + h) * D + 4 * c) = make_uint2(w0, w1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -507,10 +559,18 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, true, PD>), grid, dim3(WAVES * 64), 0, st,
                        a, n_chunks);
   } else {
-    constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
+    // Few work-groups: spread each context over more waves; many: more groups.
     dim3 grid(1, a.num_kv_heads * n_chunks, a.num_reqs);
-    hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0, st,
-                       a, n_chunks);
+    const int64_t groups = (int64_t)grid.y * grid.z;
+    if (groups < 768) {
+      constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
+      hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,
+                         st, a, n_chunks);
+    } else {
+      constexpr int WAVES = PA_DECODE_WAVES_SPLIT;
+      hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,
+                         st, a, n_chunks);
+    }
   }
   return hipGetLastError();
 }
@@ -547,11 +607,11 @@ hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits
   if (num_reqs == 0) return hipSuccess;
   dim3 grid(num_q_heads, num_reqs);
   if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, st, (uint16_t*)out, tmp_out,
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, st, (uint16_t*)out, tmp_out,
                        max_logits, exp_sums, seq_lens, num_q_heads, partition_size,
                        max_num_partitions);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, st, (uint16_t*)out, tmp_out,
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, st, (uint16_t*)out, tmp_out,
                        max_logits, exp_sums, seq_lens, num_q_heads, partition_size,
                        max_num_partitions);
   return hipGetLastError();
