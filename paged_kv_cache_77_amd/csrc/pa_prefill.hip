@@ -105,81 +105,79 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
 
-  // ---- global -> registers -> LDS staging of one 64-key tile.
-  // K: thread handles chunks u = tid + 256 i (key u / CH, chunk u % CH): rows
-  // stream contiguously.  V: key = u % 64 (lane-fast), chunk u / 64, so the
-  // transposed 2-byte LDS stores of a wave land on consecutive slots.
+  // ---- global -> registers -> LDS staging of one 64-key tile (4 blocks).
+  // K: thread chunk i is (key tid/CH + (256/CH) i, 8 elements at tid % CH), so
+  // rows stream contiguously.  V: key tid % 64 (lane-fast), chunk tid/64 + 4i,
+  // so each transposed 2-byte LDS store of a wave covers consecutive slots.
+  // All LDS offsets are loop-invariant and computed once.
   constexpr int NCH = kBN * CH / (kWaves * 64);             // chunks per thread per tensor
+  const int kc_chunk = tid % CH;
+  int k_key[NCH], k_lds[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    k_key[i] = tid / CH + (kWaves * 64 / CH) * i;
+    k_lds[i] = k_key[i] * CH + (kc_chunk ^ (k_key[i] & (CH - 1)));
+  }
+  const int v_key = tid % kBN;
+  const int v_slot = vt_slot(v_key);
+  int v_lds[8];                                             // u16 offsets for e = 0..7, chunk 0
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v_lds[e] = 64 * e + (((v_slot >> 3) ^ e) << 3) + (v_slot & 7);
+  const int v_c0 = tid / kBN;                               // chunk of i = 0; + 4 per i
+
   uint4 kreg[NCH], vreg[NCH];
+  auto load8 = [&](const uint8_t* p) -> uint4 {             // 8 elements -> 8 bf16
+    if constexpr (FP8) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p);
+      const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
+      return make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                        pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+    } else {
+      return *reinterpret_cast<const uint4*>(p);
+    }
+  };
+  const int64_t head_off = (int64_t)g * (kBlock * D);
+  const int64_t blk_stride = (int64_t)Hkv * (kBlock * D);
   auto fetch = [&](int kt) {
+    // block ids of the tile's 4 blocks (entries past the context are not read)
+    const int jb_lane = lane & 3;
+    const int32_t bid_vec = (kt * kBN + jb_lane * kBlock < seq_len) ? bt_row[kt * 4 + jb_lane] : 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      {
-        const int u = tid + kWaves * 64 * i;
-        const int key = u / CH, c = u % CH;
-        const int t = kt * kBN + key;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < seq_len) {
-          const int32_t phys = bt_row[t / kBlock];
-          const uint8_t* p = kbase + (tile_offset(phys, g, Hkv, D) + (int64_t)(t % kBlock) * D) * EB;
-          if constexpr (FP8) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(p + c * 8);
-            const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
-            v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
-          } else {
-            v = *reinterpret_cast<const uint4*>(p + c * 16);
-          }
-        }
-        kreg[i] = v;
-      }
-      {
-        const int u = tid + kWaves * 64 * i;
-        const int key = u % kBN, c = u / kBN;
-        const int t = kt * kBN + key;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < seq_len) {                                    // past the context: zero
-          const int32_t phys = bt_row[t / kBlock];
-          const uint8_t* p = vbase + (tile_offset(phys, g, Hkv, D) + (int64_t)(t % kBlock) * D) * EB;
-          if constexpr (FP8) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(p + c * 8);
-            const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
-            v = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                           pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
-          } else {
-            v = *reinterpret_cast<const uint4*>(p + c * 16);
-          }
-        }
-        vreg[i] = v;
-      }
+      const int t = kt * kBN + k_key[i];
+      const int jb = __builtin_amdgcn_readfirstlane(k_key[i] / kBlock);
+      const int32_t bid = __builtin_amdgcn_readlane(bid_vec, jb);
+      const uint8_t* p = kbase + (bid * blk_stride + head_off +
+                                  (int64_t)((k_key[i] % kBlock) * D + kc_chunk * 8)) * EB;
+      kreg[i] = t < seq_len ? load8(p) : make_uint4(0, 0, 0, 0);
+    }
+    {
+      const int t = kt * kBN + v_key;
+      const int32_t bid = __shfl(bid_vec, v_key / kBlock, kWave);
+      const uint8_t* p = vbase + (bid * blk_stride + head_off +
+                                  (int64_t)((v_key % kBlock) * D + v_c0 * 8)) * EB;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)                         // past the context: zero
+        vreg[i] = t < seq_len ? load8(p + 4 * i * 8 * EB) : make_uint4(0, 0, 0, 0);
     }
   };
   auto stage = [&](int buf) {
+    uint4* kl = &sm.k[buf][0];
     uint16_t* vt16 = reinterpret_cast<uint16_t*>(&sm.vt[buf][0]);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      {
-        const int u = tid + kWaves * 64 * i;
-        const int key = u / CH, c = u % CH;
-        sm.k[buf][key * CH + (c ^ (key & (CH - 1)))] = kreg[i];
-      }
-      {
-        const int u = tid + kWaves * 64 * i;
-        const int key = u % kBN, c = u / kBN;
-        const int slot = vt_slot(key);
-        const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+    for (int i = 0; i < NCH; ++i) kl[k_lds[i]] = kreg[i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = c * 8 + e;
-          const int chunk = (slot / 8) ^ (d & 7);
-          vt16[d * kBN + chunk * 8 + (slot % 8)] =
-              (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
-        }
-      }
+    for (int i = 0; i < NCH; ++i) {
+      uint16_t* vrow = vt16 + 512 * (v_c0 + 4 * i);
+      const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vrow[v_lds[e]] = (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
     }
   };
 
-  // ---- running state of this lane's query (keys split between lane halves)
+  // ---- running state of this lane's query (keys split between lane halves);
+  // m_run is in scaled log2 units, scores s are raw dot products.
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[DBLK];
 #pragma unroll
@@ -211,25 +209,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
           s[b] = mfma32(kf, qf[k], s[b]);
         }
       }
-      // -- scale, causal mask (select), tile max
-      const bool diag = k0 + kBN - 1 > wave_pmin;
+      // -- causal mask by select (diagonal tiles only), tile max of raw scores
+      if (k0 + kBN - 1 > wave_pmin) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int t = k0 + 32 * b + 8 * (v / 4) + 4 * lh + (v % 4);
+            s[b][v] = (t <= p_q) ? s[b][v] : -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[b][v] * qk_scale;
-          if (diag) {
-            const int t = k0 + 32 * b + 8 * (v / 4) + 4 * lh + (v % 4);
-            x = (t <= p_q) ? x : -INFINITY;
-          }
-          s[b][v] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, xor_lanes(tmax, 32));
-      // -- lazy rescale: move the max only when it grows by more than 2^8
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[b][v]);
+      tmax = fmaxf(tmax, xor_lanes(tmax, 32)) * qk_scale;
+      // -- lazy rescale: move the max only when it grows by more than 2^8.
+      // Key 0 is visible to every query, so m_run is finite after tile 0.
       if (tmax > m_run + 8.0f) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - tmax);
+        const float alpha = fast_exp2(m_run - tmax);         // 0 on the first tile
         m_run = tmax;
         l_run *= alpha;
 #pragma unroll
@@ -246,8 +245,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float x = s[b][8 * sp + e];
-            p[e] = (x == -INFINITY) ? 0.f : fast_exp2(x - m_run);
+            p[e] = fast_exp2(fmaf(s[b][8 * sp + e], qk_scale, -m_run));   // -inf -> 0
             l_run += p[e];
           }
           pf[2 * b + sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
