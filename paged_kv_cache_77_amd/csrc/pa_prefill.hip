@@ -18,7 +18,9 @@
 //       order the accumulators hold them, and V^T is stored in LDS in that
 //       order)
 // K is staged row-major with a 16-byte-chunk XOR swizzle, V transposed
-// (d-major) with the key permutation and a swizzle; both double-buffered.
+// (d-major) with the key permutation and a swizzle on d >> 1 (rows of V^T are
+// 128 bytes, so two consecutive rows share a 256-byte bank line); both
+// double-buffered.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -46,7 +48,7 @@ __device__ __forceinline__ int vt_slot(int k) {
 template <int D>
 struct PrefillSmem {
   uint4 k[2][kBN * D / 8];        // [key][16-byte chunk ^ (key & 15)]
-  uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ (d & 7)]
+  uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ ((d >> 1) & 7)]
 };
 
 template <int D, bool FP8>
@@ -122,7 +124,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
   const int v_slot = vt_slot(v_key);
   int v_lds[8];                                             // u16 offsets for e = 0..7, chunk 0
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v_lds[e] = 64 * e + (((v_slot >> 3) ^ e) << 3) + (v_slot & 7);
+  for (int e = 0; e < 8; ++e) {     // row d = 8c + e; c has the parity of v_c0
+    const int dsw = ((4 * ((tid / kBN) & 1)) + (e >> 1)) & 7;          // (d >> 1) & 7
+    v_lds[e] = 64 * e + (((v_slot >> 3) ^ dsw) << 3) + (v_slot & 7);
+  }
   const int v_c0 = tid / kBN;                               // chunk of i = 0; + 4 per i
 
   uint4 kreg[NCH], vreg[NCH];
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
         const int d = 32 * db + lq;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int chunk = (2 * ks + lh) ^ (d & 7);
+          const int chunk = (2 * ks + lh) ^ ((d >> 1) & 7);
           const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
           oacc[db] = mfma32(vf, pf[ks], oacc[db]);
         }
