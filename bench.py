@@ -2,7 +2,7 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
 One step = one pass of the hot path over one batch: slot mapping of the
-step's new tokens, their scatter into the paged cache (reshape_and_cache),
+step's new tokens and their scatter into the paged cache (one fused launch),
 then paged decode attention over every request (split-KV + merge, or a
 single pass), for the batched-decode workload (64 requests, contexts
 uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
@@ -165,7 +165,7 @@ def main() -> int:
 
     def step(timed: bool):
         if w.writes_new_kv:
-            dv.write_new_kv(d, sm[:T])
+            dv.write_new_kv_fused(d, sm[:T])      # slot mapping + scatter, one launch
         e0 = e1 = None
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)

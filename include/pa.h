@@ -108,6 +108,21 @@ int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cach
                          const int64_t* slot_mapping, void* stream);
 
 /*
+ * Slot mapping and scatter fused into one launch (the two steps above,
+ * P1 §3.1 and P3 reshape_and_cache): token j of request r (rows
+ * query_start_loc[r] .. query_start_loc[r+1]-1) lands at the slot
+ * pa_compute_slot_mapping would give it; its key/value rows are copied
+ * there bit for bit.  Requests own contiguous, increasing row ranges.
+ *  slot_mapping : int64 [num_tokens] output, or NULL when not wanted
+ * Only PA_CACHE_BF16 layouts are accepted.
+ */
+int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void* v_cache,
+                                const void* key, const void* value, const int32_t* block_table,
+                                int32_t bt_stride, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t num_reqs, int32_t num_tokens,
+                                int64_t* slot_mapping, void* stream);
+
+/*
  * Single-query decode attention (P1 §3.2: block-table walk, QK with GQA,
  * masked tail, softmax, PV; P1 §2.2: exact result via the online-softmax
  * state (m, l, A)).  For request r and query head h (g = h / G):

@@ -17,9 +17,9 @@ import torch
 __all__ = [
     "PA_CACHE_BF16", "PA_CACHE_FP8_E4M3", "PaError", "PaKvLayout", "lib", "make_layout",
     "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
-    "pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_merge_partitions",
-    "pa_prefill_varlen", "pa_debug_gather_kv", "pa_debug_fp8_to_f32",
-    "pa_validate_metadata", "EXPORTED_SYMBOLS",
+    "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
+    "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
+    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,9 +36,9 @@ PA_CACHE_FP8_E4M3 = 1
 
 EXPORTED_SYMBOLS = (
     "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
-    "pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_merge_partitions",
-    "pa_prefill_varlen", "pa_debug_gather_kv", "pa_debug_fp8_to_f32",
-    "pa_validate_metadata",
+    "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
+    "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
+    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata",
 )
 
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "pa_kv_cache_bytes": ([lp, ctypes.POINTER(ctypes.c_size_t)], _I),
             "pa_compute_slot_mapping": ([_P, _P, _I, _P, _P, _I, _I, _I, _P], _I),
             "pa_reshape_and_cache": ([lp, _P, _P, _P, _P, _I, _P, _P], _I),
+            "pa_reshape_and_cache_varlen": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P,
+                                             _P], _I),
             "pa_decode": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P], _I),
             "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
                                        _I, _I, _P, _P, _P, _P], _I),
@@ -141,6 +143,16 @@ def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping) -> 
         ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(key, "key"), _dev(value, "value"), key.shape[0],
         _dev(slot_mapping, "slot_mapping"), _stream()), "pa_reshape_and_cache")
+
+
+def pa_reshape_and_cache_varlen(layout, k_cache, v_cache, key, value, block_table,
+                                query_start_loc, seq_lens, slot_mapping=None) -> None:
+    _check(lib().pa_reshape_and_cache_varlen(
+        ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(key, "key"), _dev(value, "value"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(query_start_loc, "query_start_loc"),
+        _dev(seq_lens, "seq_lens"), seq_lens.shape[0], key.shape[0],
+        _dev(slot_mapping, "slot_mapping"), _stream()), "pa_reshape_and_cache_varlen")
 
 
 def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,

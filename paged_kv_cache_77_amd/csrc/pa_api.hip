@@ -97,6 +97,24 @@ int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cach
                                                  layout->head_dim, (hipStream_t)stream));
 }
 
+int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void* v_cache,
+                                const void* key, const void* value, const int32_t* block_table,
+                                int32_t bt_stride, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t num_reqs, int32_t num_tokens,
+                                int64_t* slot_mapping, void* stream) {
+  PA_TRY(check_layout(layout));
+  if (layout->cache_dtype != PA_CACHE_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_reqs < 0 || bt_stride <= 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0 || num_reqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !key || !value || !block_table || !query_start_loc || !seq_lens)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(key) || !aligned16(value))
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_reshape_and_cache_varlen(
+      k_cache, v_cache, key, value, block_table, bt_stride, query_start_loc, seq_lens, num_reqs,
+      num_tokens, layout->num_kv_heads, layout->head_dim, slot_mapping, (hipStream_t)stream));
+}
+
 static int decode_common(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
                          int32_t num_q_heads, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, int32_t bt_stride,

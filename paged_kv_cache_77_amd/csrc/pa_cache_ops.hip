@@ -73,6 +73,69 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* ke
   return hipGetLastError();
 }
 
+// Slot mapping and scatter in one launch: each thread copies one 16-byte
+// chunk of a (token, KV head) row and derives the token's slot itself.  The
+// request of token j is found by binary search over query_start_loc, staged
+// in LDS when it fits.
+constexpr int kQslLds = 2048;
+
+__global__ __launch_bounds__(256) void reshape_and_cache_varlen_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ key,
+    const uint4* __restrict__ value, const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ seq_lens,
+    int32_t num_reqs, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+    int64_t* __restrict__ slot_mapping) {
+  __shared__ int32_t qsl[kQslLds];
+  const bool in_lds = num_reqs + 1 <= kQslLds;
+  if (in_lds) {
+    for (int i = threadIdx.x; i <= num_reqs; i += blockDim.x) qsl[i] = query_start_loc[i];
+    __syncthreads();
+  }
+  const int chunks = head_dim / 8;
+  const int64_t per_token = (int64_t)num_kv_heads * chunks;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per_token * num_tokens) return;
+  const int j = (int)(i / per_token);
+  const int rem = (int)(i - (int64_t)j * per_token);
+  // largest r with query_start_loc[r] <= j (requests with q_len 0 are skipped)
+  int lo = 0, hi = num_reqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int v = in_lds ? qsl[mid] : query_start_loc[mid];
+    if (v <= j) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  const int q0 = in_lds ? qsl[r] : query_start_loc[r];
+  const int q1 = in_lds ? qsl[r + 1] : query_start_loc[r + 1];
+  const int pos = seq_lens[r] - (q1 - q0) + (j - q0);
+  const int logical = pos / kBlock;
+  const int64_t slot = (int64_t)block_table[(int64_t)r * bt_stride + logical] * kBlock +
+                       (pos - logical * kBlock);
+  if (slot_mapping != nullptr && rem == 0) slot_mapping[j] = slot;
+  const int g = rem / chunks;
+  const int c = rem - g * chunks;
+  const int64_t dst = slot_offset(slot, g, num_kv_heads, head_dim) / 8 + c;
+  k_cache[dst] = key[i];
+  v_cache[dst] = value[i];
+}
+
+hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const void* key,
+                                           const void* value, const int32_t* block_table,
+                                           int32_t bt_stride, const int32_t* query_start_loc,
+                                           const int32_t* seq_lens, int32_t num_reqs,
+                                           int32_t num_tokens, int32_t num_kv_heads,
+                                           int32_t head_dim, int64_t* slot_mapping,
+                                           hipStream_t stream) {
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+  if (total == 0 || num_reqs == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_varlen_kernel, dim3((uint32_t)blocks), dim3(256), 0,
+                     stream, (uint4*)k_cache, (uint4*)v_cache, (const uint4*)key,
+                     (const uint4*)value, block_table, bt_stride, query_start_loc, seq_lens,
+                     num_reqs, num_tokens, num_kv_heads, head_dim, slot_mapping);
+  return hipGetLastError();
+}
+
 // grid (ceil(max_seq_len/16), num_kv_heads, num_reqs); one row per token of
 // a block: threads copy 4-byte words of the row.
 __global__ __launch_bounds__(256) void gather_kv_kernel(

@@ -38,6 +38,14 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* ke
                                     const int64_t* slot_mapping, int32_t num_kv_heads,
                                     int32_t head_dim, hipStream_t stream);
 
+hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const void* key,
+                                           const void* value, const int32_t* block_table,
+                                           int32_t bt_stride, const int32_t* query_start_loc,
+                                           const int32_t* seq_lens, int32_t num_reqs,
+                                           int32_t num_tokens, int32_t num_kv_heads,
+                                           int32_t head_dim, int64_t* slot_mapping,
+                                           hipStream_t stream);
+
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,
                             int32_t bt_stride, const int32_t* seq_lens,

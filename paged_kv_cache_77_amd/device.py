@@ -11,7 +11,7 @@ import torch
 
 from . import (PA_CACHE_BF16, PA_CACHE_FP8_E4M3, make_layout, pa_compute_slot_mapping,
                pa_decode, pa_decode_partitioned, pa_merge_partitions, pa_prefill_varlen,
-               pa_reshape_and_cache)
+               pa_reshape_and_cache, pa_reshape_and_cache_varlen)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -85,6 +85,12 @@ def write_new_kv(d: DeviceWorkload, slot_mapping: torch.Tensor) -> None:
     """Slot mapping then scatter of this step's new tokens."""
     pa_compute_slot_mapping(slot_mapping, d.block_table, d.query_start_loc, d.seq_lens)
     pa_reshape_and_cache(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new, slot_mapping)
+
+
+def write_new_kv_fused(d: DeviceWorkload, slot_mapping: Optional[torch.Tensor] = None) -> None:
+    """The same write in one launch (slots derived in the scatter kernel)."""
+    pa_reshape_and_cache_varlen(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new,
+                                d.block_table, d.query_start_loc, d.seq_lens, slot_mapping)
 
 
 def run_decode(d: DeviceWorkload, out: torch.Tensor) -> None:

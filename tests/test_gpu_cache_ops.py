@@ -83,3 +83,33 @@ def test_gather_bit_exact(d_head, cache):
         n = int(w.seq_lens[r])
         assert np.array_equal(gk[cu[r]:cu[r + 1]], oracle.gather_kv(w.k_pool, w.block_table[r], n, 16))
         assert np.array_equal(gv[cu[r]:cu[r + 1]], oracle.gather_kv(w.v_pool, w.block_table[r], n, 16))
+
+
+@pytest.mark.parametrize("cfg,sd", [(1, None), (2, None), (4, 8)])
+def test_fused_slot_mapping_and_scatter(cfg, sd):
+    """pa_reshape_and_cache_varlen == slot mapping + scatter, bit for bit."""
+    _announce(f"fused write, config {cfg} scale_down {sd}")
+    w = wl.config_workload(cfg, scale_down=sd)
+    d = dv.to_device(w)
+    sm = torch.full((w.num_tokens,), -7, dtype=torch.int64, device="cuda")
+    dv.write_new_kv_fused(d, sm)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    assert np.array_equal(sm.cpu().numpy(), ref_sm)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
+    assert np.array_equal(dv.bits_of(d.k_cache), kp)
+    assert np.array_equal(dv.bits_of(d.v_cache), vp)
+
+
+def test_fused_write_ragged_with_empty_requests():
+    _announce("fused write, ragged with q_len 0 requests")
+    w = wl.make_workload(name="t", seq_lens=[5, 16, 0, 17, 40, 300, 33, 1],
+                         q_lens=[1, 16, 0, 3, 0, 40, 2, 1], num_q_heads=8, num_kv_heads=4,
+                         head_dim=64, seed=23, pool_blocks=60)
+    d = dv.to_device(w)
+    dv.write_new_kv_fused(d, None)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
+    assert np.array_equal(dv.bits_of(d.k_cache), kp)
+    assert np.array_equal(dv.bits_of(d.v_cache), vp)
