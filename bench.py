@@ -110,7 +110,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", choices=["auto", "split", "single"], default="auto",
+    ap.add_argument("--path", choices=["auto", "split", "single", "balanced"], default="auto",
                     help="decode path; auto = split-KV for the long-context workload, "
                          "single pass otherwise (measured faster for these batches)")
     ap.add_argument("--partition-size", type=int, default=0,
@@ -160,6 +160,7 @@ def main() -> int:
         out = torch.empty((w.num_reqs, w.num_q_heads, w.head_dim), dtype=torch.bfloat16,
                           device="cuda")
     bufs = dv.partial_buffers(d, P) if not is_prefill else None
+    ws = dv.decode_workspace(d) if args.path == "balanced" else None
     stream = torch.cuda.current_stream()
     ev = []
 
@@ -175,6 +176,8 @@ def main() -> int:
             dv.run_prefill(d, out)
         elif args.path == "single":
             dv.run_decode(d, out)
+        elif args.path == "balanced":
+            dv.run_decode_balanced(d, out, ws)
         else:
             tmp, ml, es = bufs
             pa.pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
@@ -184,7 +187,7 @@ def main() -> int:
                 e1.record(stream)
             pa.pa_merge_partitions(out, tmp, ml, es, d.seq_lens, P)
         if timed:
-            if is_prefill or args.path == "single":
+            if is_prefill or args.path in ("single", "balanced"):
                 e1.record(stream)
             ev.append((e0, e1))
 
@@ -235,6 +238,9 @@ def main() -> int:
         kbytes = nbytes["total"]
     elif args.path == "single":
         kernel = "decode_kernel (single pass)"
+        kbytes = nbytes["total"]
+    elif args.path == "balanced":
+        kernel = "decode_balanced_kernel + balanced_merge_kernel"
         kbytes = nbytes["total"]
     else:
         kernel = f"decode_kernel (split-KV, P={P})"

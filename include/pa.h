@@ -143,6 +143,29 @@ int pa_decode(const pa_kv_layout* layout, void* out, const void* q, int32_t num_
               const float* v_scale, void* stream);
 
 /*
+ * Work-balanced decode: the same result as pa_decode (P1 §2.2, §3.2), with
+ * the work split evenly over the GPU instead of one work-group per
+ * (request, KV head).  The 16-token blocks of all (request, KV head) units
+ * are laid end to end and every wave takes an equal contiguous share;
+ * units a wave covers whole are written directly, the others are split-KV
+ * pieces merged by the cross-partition formula of P1 §3.2.9 in a second
+ * launch.  Suited to batches whose context lengths differ widely.
+ *  workspace : device buffer of at least pa_decode_workspace_size() bytes,
+ *              16-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and calls that overlap on one workspace race
+ *  num_reqs  : at most 4096 (PA_ERR_UNSUPPORTED above)
+ * Other arguments as pa_decode.
+ */
+size_t pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_reqs,
+                                int32_t num_q_heads);
+int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                       int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                       int32_t max_seq_len, float scale, const float* k_scale,
+                       const float* v_scale, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Split-KV decode, first stage (P1 §3.2.7 and §3.3, the V2 partitioning).
  * Partition p of request r covers tokens [p*P, min((p+1)*P, seq_len)).
  * For every partition p < ceil(seq_lens[r]/P) and query head h writes

@@ -18,6 +18,7 @@ __all__ = [
     "PA_CACHE_BF16", "PA_CACHE_FP8_E4M3", "PaError", "PaKvLayout", "lib", "make_layout",
     "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
     "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
+    "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata", "EXPORTED_SYMBOLS",
 ]
@@ -37,6 +38,7 @@ PA_CACHE_FP8_E4M3 = 1
 EXPORTED_SYMBOLS = (
     "pa_status_string", "pa_kv_cache_bytes", "pa_compute_slot_mapping",
     "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
+    "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata",
 )
@@ -77,6 +79,9 @@ def lib() -> ctypes.CDLL:
             "pa_reshape_and_cache_varlen": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P,
                                              _P], _I),
             "pa_decode": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P], _I),
+            "pa_decode_workspace_size": ([lp, _I, _I], ctypes.c_size_t),
+            "pa_decode_balanced": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
+                                    ctypes.c_size_t, _P], _I),
             "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
                                        _I, _I, _P, _P, _P, _P], _I),
             "pa_merge_partitions": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
@@ -162,6 +167,22 @@ def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_l
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
         _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()), "pa_decode")
+
+
+def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:
+    return int(lib().pa_decode_workspace_size(ctypes.byref(layout), int(num_reqs),
+                                              int(num_q_heads)))
+
+
+def pa_decode_balanced(layout, out, q, k_cache, v_cache, block_table, seq_lens,
+                       max_seq_len: int, scale: float, workspace, k_scale=None,
+                       v_scale=None) -> None:
+    _check(lib().pa_decode_balanced(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()), "pa_decode_balanced")
 
 
 def pa_decode_partitioned(layout, q, k_cache, v_cache, block_table, seq_lens,

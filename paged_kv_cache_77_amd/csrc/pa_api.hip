@@ -174,6 +174,35 @@ int pa_decode(const pa_kv_layout* layout, void* out, const void* q, int32_t num_
   return hip_status(pa::launch_decode(a, false, (hipStream_t)stream));
 }
 
+size_t pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_reqs,
+                                int32_t num_q_heads) {
+  if (check_layout(layout) != PA_OK || check_heads(layout, num_q_heads) != PA_OK || num_reqs < 0)
+    return 0;
+  return (size_t)pa::balanced_workspace_bytes(num_reqs, num_q_heads, layout->num_kv_heads,
+                                              layout->head_dim);
+}
+
+int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                       int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                       int32_t max_seq_len, float scale, const float* k_scale,
+                       const float* v_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                       bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
+  if (num_reqs == 0) return PA_OK;
+  if (!out || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  if (num_reqs > pa::balanced_max_reqs()) return PA_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < pa_decode_workspace_size(layout, num_reqs, num_q_heads))
+    return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
+                                 block_table, bt_stride, seq_lens, max_seq_len, scale,
+                                 k_scale, v_scale);
+  a.out = out;
+  return hip_status(pa::launch_decode_balanced(a, workspace, (hipStream_t)stream));
+}
+
 int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int32_t bt_stride,

@@ -92,79 +92,48 @@ __device__ __forceinline__ Words<N> load_words(const uint8_t* p) {
 
 constexpr int kBtChunk = 1024;   // block-table entries staged in LDS at a time
 
-template <int D, int GC, bool FP8, int WAVES>
-struct DecodeSmem {
+// ---------------------------------------------------------------------------
+// One wave's decode state over a run of 16-token blocks of one (request, KV
+// head, head chunk) unit: q in registers, the online-softmax state and the
+// PV accumulators.  The kernels below differ only in how they hand out
+// blocks to waves and what they do with the finished state.
+template <int D, int GC, bool FP8>
+struct WaveDecoder {
   using S = DecodeShape<D, GC, FP8>;
-  int32_t bt[kBtChunk];
-  float p[WAVES][2][kBlock][S::GCP];
-  float m[WAVES][8];
-  float mt[WAVES][8];
-  float l[WAVES][8];
-  float acc[WAVES][GC][D];
-};
+  static constexpr int EB = S::EB, LPR = S::LPR, RK = S::RK, KCH = S::KCH, KW = S::KW,
+                       KCHB = S::KCHB, QW = S::QW, VE = S::VE, VW = S::VW, GCP = S::GCP;
+  struct Tile {
+    Words<KW> k[RK][KCH];
+    Words<VW> v[4];
+  };
 
-// PART: false -> write the final bf16 output; true -> write the partition
-// partials.  QSL: q/out rows come from query_start_loc (varlen decode rows).
-template <int D, int GC, bool FP8, int WAVES, bool PART, int PD>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_chunks) {
-  using S = DecodeShape<D, GC, FP8>;
-  constexpr int EB = S::EB, LPR = S::LPR, RK = S::RK, KCH = S::KCH, KW = S::KW,
-                KCHB = S::KCHB, QW = S::QW, VE = S::VE, VW = S::VW;
-  __shared__ DecodeSmem<D, GC, FP8, WAVES> sm;
-
-  const int r = blockIdx.z;
-  const int g = blockIdx.y / n_chunks;
-  const int hc = blockIdx.y - g * n_chunks;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int h0 = g * G + hc * GC;                 // first query head of the chunk
-  const int nh = min(GC, G - hc * GC);            // real heads in the chunk
-
-  // query / output row of this request
-  int row_q = r;
-  if (a.query_start_loc != nullptr) {
-    const int lo = a.query_start_loc[r];
-    if (a.query_start_loc[r + 1] - lo != 1) return;   // not a decode row
-    row_q = lo;
-  }
-  const int seq_len = a.seq_lens[r];
-  int t_begin = 0, t_end = seq_len;
-  if constexpr (PART) {
-    t_begin = blockIdx.x * a.partition_size;
-    if (t_begin >= seq_len) return;
-    t_end = min(seq_len, t_begin + a.partition_size);
-  }
-
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int lane = tid % kWave;
-
-  if (t_end <= t_begin) {                         // empty context: zero row
-    if constexpr (!PART) {
-      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-      for (int i = tid; i < nh * D; i += WAVES * kWave)
-        out[((int64_t)row_q * a.num_q_heads + h0 + i / D) * D + (i % D)] = 0;
-    }
-    return;
-  }
-
-  // ---- per-lane roles
-  const int kc = lane % LPR;                      // K lane within its row
-  const int krow0 = lane / LPR;                   // first K row; rows krow0 + (64/LPR)*i
-  const int vrg = lane / 16;                      // V row group; rows vrg + 4*i
-  const int vcol = (lane % 16) * VE;              // first V element of this lane
-
-  // ---- q for the chunk's heads, in this lane's K element positions
+  int lane, kc, krow0, vrg, vcol;
+  int nh;                        // real heads of the current unit's chunk
+  float qk_scale;
   uint32_t qreg[GC][QW];
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  float m_run, m_true, l_part;   // lazy max (log2 units), exact max, exp-sum: head kc
+  float acc[GC][VE];
+
+  __device__ __forceinline__ void init(int lane_, float qk_scale_) {
+    lane = lane_;
+    kc = lane % LPR;             // K lane within its row
+    krow0 = lane / LPR;          // first K row; rows krow0 + (64/LPR)*i
+    vrg = lane / 16;             // V row group; rows vrg + 4*i
+    vcol = (lane % 16) * VE;     // first V element of this lane
+    qk_scale = qk_scale_;
+  }
+
+  // q of query row `row_q`, heads h0 .. h0+nh-1, at this lane's K positions
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row_q, int num_q_heads,
+                                         int h0, int nh_) {
+    nh = nh_;
+    constexpr int CE = KCHB / EB;            // elements per K chunk
 #pragma unroll
     for (int j = 0; j < GC; ++j) {
       const bool real = j < nh;
-      const uint16_t* qh = q + ((int64_t)row_q * a.num_q_heads + h0 + (real ? j : 0)) * D;
+      const uint16_t* qh = q + (row_q * num_q_heads + h0 + (real ? j : 0)) * D;
 #pragma unroll
       for (int k = 0; k < KCH; ++k) {
-        // elements of chunk (kc + LPR*k): KCHB/EB of them
-        constexpr int CE = KCHB / EB;
         const int e0 = (kc + LPR * k) * CE;
 #pragma unroll
         for (int u = 0; u < CE / 2; ++u) {
@@ -175,34 +144,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
     }
   }
 
-  float qk_scale = a.scale * kLog2e;
-  if constexpr (FP8) qk_scale *= *a.k_scale;
-
-  // ---- block range of the work-group
-  const int first_block = t_begin / kBlock;
-  const int last_block = (t_end - 1) / kBlock;
-  const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
-
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
-  const int Hkv = a.num_kv_heads;
-
-  float m_run = -INFINITY;       // lazy running max (log2 units) of head kc
-  float m_true = -INFINITY;      // exact max of this lane's scores of head kc
-  float l_part = 0.f;            // exp-sum of head kc over this lane's rows
-  float acc[GC][VE];
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    m_true = -INFINITY;
+    l_part = 0.f;
 #pragma unroll
-  for (int j = 0; j < GC; ++j)
+    for (int j = 0; j < GC; ++j)
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[j][e] = 0.f;
+      for (int e = 0; e < VE; ++e) acc[j][e] = 0.f;
+  }
 
-  struct Tile {
-    Words<KW> k[RK][KCH];
-    Words<VW> v[4];
-  };
-
-  auto load_tile = [&](Tile& t, int32_t phys) {
-    const int64_t off = tile_offset(phys, g, Hkv, D) * EB;
+  __device__ __forceinline__ void load_tile(Tile& t, const uint8_t* kbase, const uint8_t* vbase,
+                                            int32_t phys, int g, int num_kv_heads) const {
+    const int64_t off = tile_offset(phys, g, num_kv_heads, D) * EB;
     const uint8_t* kt = kbase + off;
     const uint8_t* vt = vbase + off;
 #pragma unroll
@@ -214,9 +168,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       t.v[i] = load_words<VW>(vt + ((vrg + 4 * i) * D + vcol) * EB);
-  };
+  }
 
-  auto compute = [&](Tile& t, int tok0, int buf) {
+  // Fold one block (tokens tok0 .. tok0+15, those >= t_end excluded) into
+  // the state.  `slab` is this wave's [16][GCP] float LDS buffer.
+  __device__ __forceinline__ void compute(const Tile& t, int tok0, int t_end, float* slab) {
     // -- scores of the chunk's heads for this lane's K rows
     float s[RK][GC];
 #pragma unroll
@@ -290,12 +246,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
       }
     }
     // -- probabilities to the LDS slab
-    float* slab = &sm.p[w][buf][0][0];
 #pragma unroll
     for (int i = 0; i < RK; ++i) {
       const float p = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
       l_part += p;
-      if (kc < GC) slab[(krow0 + (64 / LPR) * i) * S::GCP + kc] = p;
+      if (kc < GC) slab[(krow0 + (64 / LPR) * i) * GCP + kc] = p;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -305,10 +260,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = vrg + 4 * i;
-      float pv[S::GCP];
+      float pv[GCP];
 #pragma unroll
-      for (int q4 = 0; q4 < S::GCP / 4; ++q4) {
-        const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&slab[vr * S::GCP + q4 * 4]);
+      for (int q4 = 0; q4 < GCP / 4; ++q4) {
+        const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&slab[vr * GCP + q4 * 4]);
         pv[q4 * 4 + 0] = p4.x; pv[q4 * 4 + 1] = p4.y;
         pv[q4 * 4 + 2] = p4.z; pv[q4 * 4 + 3] = p4.w;
       }
@@ -336,61 +291,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[j][e] = fmaf(pv[j], vf[e], acc[j][e]);
     }
-  };
-
-  // Walk the range in chunks of kBtChunk blocks whose block-table entries are
-  // staged in LDS.  Within a chunk each wave double-buffers its tiles; the
-  // prefetch is unconditional (the index is clamped to the wave's last block,
-  // a repeat read that hits in L2) so every iteration has the same loads in
-  // flight and the compiler's wait counts stay exact.
-  for (int cb = first_block; cb <= last_block; cb += kBtChunk) {
-    const int nb = min(last_block + 1 - cb, kBtChunk);
-    __syncthreads();
-    for (int i = tid; i < nb; i += WAVES * kWave) sm.bt[i] = bt_row[cb + i];
-    __syncthreads();
-    const int n = nb > w ? (nb - w + WAVES - 1) / WAVES : 0;   // this wave's blocks
-    if (n > 0) {
-      auto phys_of = [&](int it) {
-        return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * WAVES]);
-      };
-      auto tok0_of = [&](int it) { return (cb + w + it * WAVES) * kBlock; };
-      if constexpr (PD == 1) {
-        Tile ta, tb;
-        load_tile(ta, phys_of(0));
-        int32_t pn = phys_of(1);
-        for (int it = 0; it < n; it += 2) {
-          load_tile(tb, pn);
-          pn = phys_of(it + 2);
-          compute(ta, tok0_of(it), 0);
-          if (it + 1 >= n) break;
-          load_tile(ta, pn);
-          pn = phys_of(it + 3);
-          compute(tb, tok0_of(it + 1), 1);
-        }
-      } else {                                  // two tiles in flight while computing
-        Tile t0, t1, t2;
-        load_tile(t0, phys_of(0));
-        load_tile(t1, phys_of(1));
-        int32_t pn = phys_of(2);
-        for (int it = 0; it < n; it += 3) {
-          load_tile(t2, pn);
-          pn = phys_of(it + 3);
-          compute(t0, tok0_of(it), it & 1);
-          if (it + 1 >= n) break;
-          load_tile(t0, pn);
-          pn = phys_of(it + 4);
-          compute(t1, tok0_of(it + 1), (it + 1) & 1);
-          if (it + 2 >= n) break;
-          load_tile(t1, pn);
-          pn = phys_of(it + 5);
-          compute(t2, tok0_of(it + 2), it & 1);
-        }
-      }
-    }
   }
 
-  // ---- wave totals: l over the rows of head kc, acc over the 4 row groups
-  {
+  // Reduce the lane partials: afterwards lane j < GC holds head j's m_run,
+  // m_true and l_part, and lanes 0..15 hold acc[j][vcol + e] summed over rows.
+  __device__ __forceinline__ void finish() {
     float l = l_part, mt = m_true;
     if constexpr (LPR == 4) {
       l += dpp<kRowRor4>(l);
@@ -414,16 +319,147 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
         acc[j][e] = v;
       }
   }
+};
+
+// Stream n blocks through the decoder with PD tiles in flight.  phys_of(it)
+// must accept it >= n (clamped by the caller) so the prefetch is
+// unconditional and the compiler's wait counts stay exact.
+template <int PD, class Dec, class PhysFn, class TokFn>
+__device__ __forceinline__ void stream_blocks(Dec& dec, int n, const uint8_t* kbase,
+                                              const uint8_t* vbase, int g, int num_kv_heads,
+                                              int t_end, float* slab0, float* slab1,
+                                              PhysFn phys_of, TokFn tok0_of) {
+  using Tile = typename Dec::Tile;
+  if constexpr (PD == 1) {
+    Tile ta, tb;
+    dec.load_tile(ta, kbase, vbase, phys_of(0), g, num_kv_heads);
+    int32_t pn = phys_of(1);
+    for (int it = 0; it < n; it += 2) {
+      dec.load_tile(tb, kbase, vbase, pn, g, num_kv_heads);
+      pn = phys_of(it + 2);
+      dec.compute(ta, tok0_of(it), t_end, slab0);
+      if (it + 1 >= n) break;
+      dec.load_tile(ta, kbase, vbase, pn, g, num_kv_heads);
+      pn = phys_of(it + 3);
+      dec.compute(tb, tok0_of(it + 1), t_end, slab1);
+    }
+  } else {                                  // two tiles in flight while computing
+    Tile t0, t1, t2;
+    dec.load_tile(t0, kbase, vbase, phys_of(0), g, num_kv_heads);
+    dec.load_tile(t1, kbase, vbase, phys_of(1), g, num_kv_heads);
+    int32_t pn = phys_of(2);
+    for (int it = 0; it < n; it += 3) {
+      dec.load_tile(t2, kbase, vbase, pn, g, num_kv_heads);
+      pn = phys_of(it + 3);
+      dec.compute(t0, tok0_of(it), t_end, (it & 1) ? slab1 : slab0);
+      if (it + 1 >= n) break;
+      dec.load_tile(t0, kbase, vbase, pn, g, num_kv_heads);
+      pn = phys_of(it + 4);
+      dec.compute(t1, tok0_of(it + 1), t_end, (it & 1) ? slab0 : slab1);
+      if (it + 2 >= n) break;
+      dec.load_tile(t1, kbase, vbase, pn, g, num_kv_heads);
+      pn = phys_of(it + 5);
+      dec.compute(t2, tok0_of(it + 2), t_end, (it & 1) ? slab1 : slab0);
+    }
+  }
+}
+
+template <int D, int GC, bool FP8, int WAVES>
+struct DecodeSmem {
+  using S = DecodeShape<D, GC, FP8>;
+  int32_t bt[kBtChunk];
+  float p[WAVES][2][kBlock][S::GCP];
+  float m[WAVES][8];
+  float mt[WAVES][8];
+  float l[WAVES][8];
+  float acc[WAVES][GC][D];
+};
+
+// One work-group per (request, KV head, head chunk[, partition]).
+// PART: false -> write the final bf16 output; true -> write the partition
+// partials.  Rows of varlen batches come from query_start_loc when given.
+template <int D, int GC, bool FP8, int WAVES, bool PART, int PD>
+__global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_chunks) {
+  using Dec = WaveDecoder<D, GC, FP8>;
+  __shared__ DecodeSmem<D, GC, FP8, WAVES> sm;
+
+  const int r = blockIdx.z;
+  const int g = blockIdx.y / n_chunks;
+  const int hc = blockIdx.y - g * n_chunks;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h0 = g * G + hc * GC;                 // first query head of the chunk
+  const int nh = min(GC, G - hc * GC);            // real heads in the chunk
+
+  // query / output row of this request
+  int row_q = r;
+  if (a.query_start_loc != nullptr) {
+    const int lo = a.query_start_loc[r];
+    if (a.query_start_loc[r + 1] - lo != 1) return;   // not a decode row
+    row_q = lo;
+  }
+  const int seq_len = a.seq_lens[r];
+  int t_begin = 0, t_end = seq_len;
+  if constexpr (PART) {
+    t_begin = blockIdx.x * a.partition_size;
+    if (t_begin >= seq_len) return;
+    t_end = min(seq_len, t_begin + a.partition_size);
+  }
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+
+  if (t_end <= t_begin) {                         // empty context: zero row
+    if constexpr (!PART) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+      for (int i = tid; i < nh * D; i += WAVES * kWave)
+        out[((int64_t)row_q * a.num_q_heads + h0 + i / D) * D + (i % D)] = 0;
+    }
+    return;
+  }
+
+  float qk_scale = a.scale * kLog2e;
+  if constexpr (FP8) qk_scale *= *a.k_scale;
+  Dec dec;
+  dec.init(lane, qk_scale);
+  dec.load_q(reinterpret_cast<const uint16_t*>(a.q), row_q, a.num_q_heads, h0, nh);
+  dec.reset();
+
+  const int first_block = t_begin / kBlock;
+  const int last_block = (t_end - 1) / kBlock;
+  const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+
+  // Walk the range in chunks of kBtChunk blocks whose block-table entries are
+  // staged in LDS; wave w takes every WAVES-th block of a chunk.
+  for (int cb = first_block; cb <= last_block; cb += kBtChunk) {
+    const int nb = min(last_block + 1 - cb, kBtChunk);
+    __syncthreads();
+    for (int i = tid; i < nb; i += WAVES * kWave) sm.bt[i] = bt_row[cb + i];
+    __syncthreads();
+    const int n = nb > w ? (nb - w + WAVES - 1) / WAVES : 0;   // this wave's blocks
+    if (n > 0) {
+      stream_blocks<PD>(
+          dec, n, kbase, vbase, g, a.num_kv_heads, t_end, &sm.p[w][0][0][0], &sm.p[w][1][0][0],
+          [&](int it) {
+            return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * WAVES]);
+          },
+          [&](int it) { return (cb + w + it * WAVES) * kBlock; });
+    }
+  }
+
+  dec.finish();
   if (lane < GC) {                    // lane j: row 0, kc == j
-    sm.m[w][lane] = m_run;
-    sm.mt[w][lane] = m_true;
-    sm.l[w][lane] = l_part;
+    sm.m[w][lane] = dec.m_run;
+    sm.mt[w][lane] = dec.m_true;
+    sm.l[w][lane] = dec.l_part;
   }
   if (lane < 16) {
 #pragma unroll
     for (int j = 0; j < GC; ++j)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sm.acc[w][j][vcol + e] = acc[j][e];
+      for (int e = 0; e < Dec::VE; ++e) sm.acc[w][j][dec.vcol + e] = dec.acc[j][e];
   }
   __syncthreads();
 
@@ -459,6 +495,237 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
           f32_to_bf16(O);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Work-balanced decode.  The items are the 16-token blocks of every unit
+// (request r, KV head g, head chunk), units in order and blocks in order
+// within a unit; with N items and W waves, wave k takes items
+// [floor(kN/W), floor((k+1)N/W)).  A unit a wave covers entirely is written
+// to the output directly.  Otherwise the wave leaves a partial record --
+// slot 0 for a piece that does not start at the unit's first block (only the
+// wave's first piece can), slot 1 for a piece that starts there but ends
+// inside the unit (only its last piece can) -- and balanced_merge_kernel
+// folds the pieces of each split unit with the merge of the split-KV page
+// section (§3.2.9).  Every wave streams the same number of blocks, so no
+// long request leaves the GPU idle at the end.
+constexpr int kBalWaves = 4;               // waves per work-group
+constexpr int kBalMaxReqs = 4096;          // requests whose prefix fits in LDS
+constexpr int kBalMaxTotalWaves = 4096;    // waves the workspace is sized for
+constexpr int kBalSegBlocks = 256;         // block-table entries per wave in LDS
+
+struct BalancedLayout {
+  // workspace: int32 prefix[R + 1] (256-byte aligned), then float records
+  // [W][2][GC][D + 2]: m (natural log units) per head, l per head, O rows.
+  static __host__ __device__ int64_t header_bytes(int num_reqs) {
+    return ((int64_t)(num_reqs + 1) * 4 + 255) / 256 * 256;
+  }
+  static __host__ __device__ int64_t record_floats(int gc, int d) { return (int64_t)gc * (d + 2); }
+};
+
+__device__ __forceinline__ int64_t bal_bound(int64_t k, int64_t N, int64_t W) {
+  return k * N / W;
+}
+
+// Number of blocks of every request, exclusive prefix into C[0..R] (LDS).
+__device__ __forceinline__ void block_prefix(const int32_t* seq_lens, int R, int32_t* C,
+                                             int32_t* scratch256) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (R + nt - 1) / nt;
+  const int lo = min(R, tid * per), hi = min(R, lo + per);
+  int32_t sum = 0;
+  for (int r = lo; r < hi; ++r) sum += (seq_lens[r] + kBlock - 1) / kBlock;
+  scratch256[tid] = sum;
+  __syncthreads();
+  for (int s = 1; s < nt; s <<= 1) {          // inclusive Hillis-Steele scan
+    const int32_t v = tid >= s ? scratch256[tid - s] : 0;
+    __syncthreads();
+    scratch256[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = scratch256[tid] - sum;         // exclusive prefix of this chunk
+  for (int r = lo; r < hi; ++r) {
+    C[r] = run;
+    run += (seq_lens[r] + kBlock - 1) / kBlock;
+  }
+  if (tid == nt - 1) C[R] = scratch256[nt - 1];
+  __syncthreads();
+}
+
+template <int D, int GC, bool FP8, int PD>
+__global__ __launch_bounds__(kBalWaves * 64) void decode_balanced_kernel(
+    DecodeArgs a, int n_chunks, float* __restrict__ records, int32_t* __restrict__ prefix_out) {
+  using Dec = WaveDecoder<D, GC, FP8>;
+  __shared__ int32_t C[kBalMaxReqs + 1];
+  __shared__ int32_t scan[kBalWaves * 64];
+  __shared__ int32_t bt_l[kBalWaves][kBalSegBlocks];
+  __shared__ float slab[kBalWaves][2][kBlock][Dec::GCP];
+
+  const int R = a.num_reqs;
+  block_prefix(a.seq_lens, R, C, scan);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= R; i += blockDim.x) prefix_out[i] = C[i];
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int U = a.num_kv_heads * n_chunks;                  // units per request
+  const int64_t N = (int64_t)C[R] * U;
+  const int64_t W = (int64_t)gridDim.x * kBalWaves;
+  const int64_t k = (int64_t)blockIdx.x * kBalWaves + w;
+  const int64_t x_end = bal_bound(k + 1, N, W);
+  int64_t x = bal_bound(k, N, W);
+  const int64_t x_begin = x;
+  int piece_b0 = 0;
+
+  float qk_scale = a.scale * kLog2e;
+  if constexpr (FP8) qk_scale *= *a.k_scale;
+  Dec dec;
+  dec.init(lane, qk_scale);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  const float vs = FP8 ? *a.v_scale : 1.f;
+  const int rec = (int)BalancedLayout::record_floats(GC, D);
+
+  while (x < x_end) {
+    // unit containing item x: the largest r with C[r]*U <= x (requests with
+    // no blocks share their C with the next one and are never picked)
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)C[mid] * U <= x) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int nb = C[r + 1] - C[r];
+    const int64_t local = x - (int64_t)C[r] * U;
+    const int j = (int)(local / nb);
+    const int b0 = (int)(local - (int64_t)j * nb);
+    const int b1 = (int)min<int64_t>(nb, b0 + (x_end - x));
+    const int g = j / n_chunks, hc = j - g * n_chunks;
+    const int h0 = g * G + hc * GC, nh = min(GC, G - hc * GC);
+    const int seq_len = a.seq_lens[r];
+    const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
+
+    if (b0 == 0 || x == x_begin) {
+      piece_b0 = b0;            // a new unit (or the wave's first piece)
+      dec.load_q(reinterpret_cast<const uint16_t*>(a.q), r, a.num_q_heads, h0, nh);
+      dec.reset();
+    }
+    // at most kBalSegBlocks blocks per pass; the unit continues in the next pass
+    const int ce = min(b1, b0 + kBalSegBlocks);
+    {
+      const int n = ce - b0;
+      for (int i = lane; i < n; i += kWave) bt_l[w][i] = bt_row[b0 + i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      stream_blocks<PD>(
+          dec, n, kbase, vbase, g, a.num_kv_heads, seq_len, &slab[w][0][0][0], &slab[w][1][0][0],
+          [&](int it) { return __builtin_amdgcn_readfirstlane(bt_l[w][min(it, n - 1)]); },
+          [&](int it) { return (b0 + it) * kBlock; });
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (ce < b1) {                            // more of this piece to come
+      x += ce - b0;
+      continue;
+    }
+    dec.finish();
+
+    if (piece_b0 == 0 && b1 == nb) {                // the whole unit: write the output row
+#pragma unroll
+      for (int jj = 0; jj < GC; ++jj) {
+        const float inv = vs / __builtin_bit_cast(float,
+            __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec.l_part), jj));
+        if (jj < nh && lane < 16) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) +
+                        ((int64_t)r * a.num_q_heads + h0 + jj) * D + dec.vcol;
+#pragma unroll
+          for (int e = 0; e < Dec::VE; ++e) o[e] = f32_to_bf16(dec.acc[jj][e] * inv);
+        }
+      }
+    } else {                                  // a piece: partial record
+      const int slot = piece_b0 != 0 ? 0 : 1;
+      float* rp = records + (k * 2 + slot) * rec;
+#pragma unroll
+      for (int jj = 0; jj < GC; ++jj) {
+        const float L = __builtin_bit_cast(float,
+            __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec.l_part), jj));
+        const float M = __builtin_bit_cast(float,
+            __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec.m_run), jj));
+        const float Mt = __builtin_bit_cast(float,
+            __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec.m_true), jj));
+        const float inv = vs / L;
+        if (lane == 0) {
+          rp[jj] = Mt * kLn2;                               // m in natural-log units
+          rp[GC + jj] = L * fast_exp2(M - Mt);             // l relative to it
+        }
+        if (lane < 16) {
+#pragma unroll
+          for (int e = 0; e < Dec::VE; ++e) rp[2 * GC + jj * D + dec.vcol + e] = dec.acc[jj][e] * inv;
+        }
+      }
+    }
+    x += b1 - b0;
+  }
+}
+
+// Fold the pieces of every split unit.  One work-group per unit, one wave
+// per head of the chunk: lanes first read the pieces' (m, l) in parallel,
+// then every lane sums its D/64 output elements over the pieces.
+template <int D, int GC>
+__global__ __launch_bounds__(GC * 64) void balanced_merge_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ records,
+    const int32_t* __restrict__ prefix, int32_t num_reqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t n_chunks, int32_t total_waves) {
+  constexpr int E = D / 64;
+  const int U = num_kv_heads * n_chunks;
+  const int r = blockIdx.x / U, j = blockIdx.x - (blockIdx.x / U) * U;
+  const int lane = threadIdx.x % 64, jj = threadIdx.x / 64;
+  const int G = num_q_heads / num_kv_heads;
+  const int g = j / n_chunks, hc = j - g * n_chunks;
+  const int h0 = g * G + hc * GC, nh = min(GC, G - hc * GC);
+  if (jj >= nh) return;
+  const int nb = prefix[r + 1] - prefix[r];
+  uint16_t* o = out + ((int64_t)r * num_q_heads + h0 + jj) * D;
+  if (nb == 0) {                                    // empty context: zero row
+    for (int i = lane; i < D; i += 64) o[i] = 0;
+    return;
+  }
+  const int64_t N = (int64_t)prefix[num_reqs] * U;
+  const int64_t W = total_waves;
+  const int64_t S = (int64_t)prefix[r] * U + (int64_t)j * nb;
+  const int64_t Eend = S + nb;
+  // wave holding item x: the largest k with floor(kN/W) <= x
+  auto wave_of = [&](int64_t xx) { return ((xx + 1) * W + N - 1) / N - 1; };
+  const int64_t kf = wave_of(S), kl = wave_of(Eend - 1);
+  if (kf == kl) return;                             // written whole by one wave
+  const int rec = (int)BalancedLayout::record_floats(GC, D);
+  const int npieces = (int)(kl - kf + 1);
+  // pass 1: max of the pieces' m (lanes over pieces)
+  float M = -INFINITY;
+  for (int i = lane; i < npieces; i += 64) {
+    const int64_t kk = kf + i;
+    if (kk > kf && bal_bound(kk, N, W) == bal_bound(kk + 1, N, W)) continue;   // empty wave
+    M = fmaxf(M, records[(kk * 2 + (kk == kf ? 1 : 0)) * rec + jj]);
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, xor_lanes(M, s));
+  // pass 2: weighted sum of the pieces' rows
+  float L = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int i = 0; i < npieces; ++i) {
+    const int64_t kk = kf + i;
+    if (kk > kf && bal_bound(kk, N, W) == bal_bound(kk + 1, N, W)) continue;
+    const float* rp = records + (kk * 2 + (kk == kf ? 1 : 0)) * rec;
+    const float wgt = rp[GC + jj] * fast_exp2((rp[jj] - M) * kLog2e);
+    L += wgt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, rp[2 * GC + jj * D + lane * E + e], acc[e]);
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[lane * E + e] = f32_to_bf16(acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -575,30 +842,83 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
-static hipError_t launch_decode_d(const DecodeArgs& a, bool partitioned, hipStream_t st) {
+template <int D, int GC, bool FP8>
+static hipError_t launch_balanced_t(const DecodeArgs& a, void* workspace, hipStream_t st) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  switch (G) {
-    case 1: return launch_decode_t<D, 1, FP8>(a, partitioned, st);
-    case 2: return launch_decode_t<D, 2, FP8>(a, partitioned, st);
-    case 3: return launch_decode_t<D, 3, FP8>(a, partitioned, st);
-    case 4: return launch_decode_t<D, 4, FP8>(a, partitioned, st);
-    case 5: return launch_decode_t<D, 5, FP8>(a, partitioned, st);
-    case 6: return launch_decode_t<D, 6, FP8>(a, partitioned, st);
-    case 7: return launch_decode_t<D, 7, FP8>(a, partitioned, st);
-    default: return launch_decode_t<D, 8, FP8>(a, partitioned, st);   // chunks of 8
-  }
+  const int n_chunks = (G + GC - 1) / GC;
+  constexpr int PD = PA_DECODE_PREFETCH;
+  auto kern = decode_balanced_kernel<D, GC, FP8, PD>;
+  // as many waves as fit on the device at once (one round, no tail)
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBalWaves * 64, 0);
+  if (e != hipSuccess) return e;
+  int groups = max(1, cus * max(1, per_cu));
+  groups = min(groups, kBalMaxTotalWaves / kBalWaves);
+  int32_t* prefix = reinterpret_cast<int32_t*>(workspace);
+  float* records = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                            BalancedLayout::header_bytes(a.num_reqs));
+  hipLaunchKernelGGL(kern, dim3(groups), dim3(kBalWaves * 64), 0, st, a, n_chunks, records, prefix);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int units = a.num_reqs * a.num_kv_heads * n_chunks;
+  hipLaunchKernelGGL((balanced_merge_kernel<D, GC>), dim3(units), dim3(GC * 64), 0, st,
+                     reinterpret_cast<uint16_t*>(a.out), records, prefix, a.num_reqs,
+                     a.num_q_heads, a.num_kv_heads, n_chunks, groups * kBalWaves);
+  return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool partitioned, hipStream_t st) {
+template <int D, bool FP8>
+static hipError_t launch_decode_d(const DecodeArgs& a, int mode, void* ws, hipStream_t st) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+#define PA_CASE(GCV)                                                              \
+  case GCV:                                                                       \
+    return mode == 2 ? launch_balanced_t<D, GCV, FP8>(a, ws, st)                  \
+                     : launch_decode_t<D, GCV, FP8>(a, mode == 1, st);
+  switch (G) {
+    PA_CASE(1)
+    PA_CASE(2)
+    PA_CASE(3)
+    PA_CASE(4)
+    PA_CASE(5)
+    PA_CASE(6)
+    PA_CASE(7)
+    default:                                                  // chunks of 8
+      return mode == 2 ? launch_balanced_t<D, 8, FP8>(a, ws, st)
+                       : launch_decode_t<D, 8, FP8>(a, mode == 1, st);
+  }
+#undef PA_CASE
+}
+
+static hipError_t launch_any(const DecodeArgs& a, int mode, void* ws, hipStream_t st) {
   if (a.num_reqs == 0) return hipSuccess;
   const bool fp8 = a.cache_dtype != 0;
   if (a.head_dim == 64)
-    return fp8 ? launch_decode_d<64, true>(a, partitioned, st)
-               : launch_decode_d<64, false>(a, partitioned, st);
-  return fp8 ? launch_decode_d<128, true>(a, partitioned, st)
-             : launch_decode_d<128, false>(a, partitioned, st);
+    return fp8 ? launch_decode_d<64, true>(a, mode, ws, st)
+               : launch_decode_d<64, false>(a, mode, ws, st);
+  return fp8 ? launch_decode_d<128, true>(a, mode, ws, st)
+             : launch_decode_d<128, false>(a, mode, ws, st);
 }
+
+hipError_t launch_decode(const DecodeArgs& a, bool partitioned, hipStream_t st) {
+  return launch_any(a, partitioned ? 1 : 0, nullptr, st);
+}
+
+hipError_t launch_decode_balanced(const DecodeArgs& a, void* workspace, hipStream_t st) {
+  return launch_any(a, 2, workspace, st);
+}
+
+int64_t balanced_workspace_bytes(int num_reqs, int num_q_heads, int num_kv_heads, int head_dim) {
+  const int G = num_q_heads / num_kv_heads;
+  const int gc = G > 8 ? 8 : G;
+  return BalancedLayout::header_bytes(num_reqs) +
+         (int64_t)kBalMaxTotalWaves * 2 * BalancedLayout::record_floats(gc, head_dim) * 4;
+}
+
+int balanced_max_reqs() { return kBalMaxReqs; }
 
 hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,

@@ -60,6 +60,12 @@ hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
 // request and KV head); true writes the partials.
 hipError_t launch_decode(const DecodeArgs& args, bool partitioned, hipStream_t stream);
 
+// Work-balanced decode (output as launch_decode's single pass) and its
+// workspace size in bytes; at most balanced_max_reqs() requests.
+hipError_t launch_decode_balanced(const DecodeArgs& args, void* workspace, hipStream_t stream);
+int64_t balanced_workspace_bytes(int num_reqs, int num_q_heads, int num_kv_heads, int head_dim);
+int balanced_max_reqs();
+
 hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

@@ -11,7 +11,8 @@ import torch
 
 from . import (PA_CACHE_BF16, PA_CACHE_FP8_E4M3, make_layout, pa_compute_slot_mapping,
                pa_decode, pa_decode_partitioned, pa_merge_partitions, pa_prefill_varlen,
-               pa_reshape_and_cache, pa_reshape_and_cache_varlen)
+               pa_reshape_and_cache, pa_reshape_and_cache_varlen, pa_decode_balanced,
+               pa_decode_workspace_size)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -96,6 +97,18 @@ def write_new_kv_fused(d: DeviceWorkload, slot_mapping: Optional[torch.Tensor] =
 def run_decode(d: DeviceWorkload, out: torch.Tensor) -> None:
     pa_decode(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
               d.max_seq_len, float(d.w.scale), d.k_scale, d.v_scale)
+
+
+def decode_workspace(d: DeviceWorkload) -> torch.Tensor:
+    n = pa_decode_workspace_size(d.layout, d.w.num_reqs, d.w.num_q_heads)
+    return torch.empty((n,), dtype=torch.uint8, device=d.q.device)
+
+
+def run_decode_balanced(d: DeviceWorkload, out: torch.Tensor, ws=None) -> torch.Tensor:
+    ws = decode_workspace(d) if ws is None else ws
+    pa_decode_balanced(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                       d.max_seq_len, float(d.w.scale), ws, d.k_scale, d.v_scale)
+    return ws
 
 
 def run_decode_partitioned(d: DeviceWorkload, out: torch.Tensor, partition_size: int,

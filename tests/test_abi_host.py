@@ -125,3 +125,19 @@ def test_validate_metadata():
     qsl[2] = 0
     assert pa.pa_validate_metadata(w.block_table, qsl, w.seq_lens, None,
                                    w.num_blocks) == pa.PA_ERR_METADATA
+
+
+def test_balanced_workspace_size_and_checks():
+    L = pa.lib()
+    lay = pa.make_layout(100, 8, 128, 0)
+    n = pa.pa_decode_workspace_size(lay, 64, 32)
+    assert n >= 4 * 65 and n % 4 == 0
+    assert pa.pa_decode_workspace_size(pa.make_layout(100, 8, 96, 0), 64, 32) == 0
+    p = ctypes.c_void_p(1024)
+    # workspace too small -> invalid argument, nothing launched
+    assert L.pa_decode_balanced(ctypes.byref(lay), p, p, 64, 32, p, p, p, 256, p, 4096, 0.1,
+                                None, None, p, n - 16, None) == pa.PA_ERR_INVALID_ARG
+    # too many requests for the balanced schedule
+    big = pa.pa_decode_workspace_size(lay, 5000, 32)
+    assert L.pa_decode_balanced(ctypes.byref(lay), p, p, 5000, 32, p, p, p, 256, p, 4096, 0.1,
+                                None, None, p, big, None) == pa.PA_ERR_UNSUPPORTED

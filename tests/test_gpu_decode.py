@@ -64,6 +64,10 @@ def test_decode_shapes(hq, hkv, d, cache):
     dv.run_decode(dd, out)
     torch.cuda.synchronize()
     check_bf16(dv.bits_of(out), ref, "pa_decode")
+    outb = _out(w)
+    dv.run_decode_balanced(dd, outb)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(outb), ref, "pa_decode_balanced")
     for P in (16, 64, 512):
         out2 = _out(w)
         tmp, ml, es = dv.run_decode_partitioned(dd, out2, P)
@@ -93,9 +97,12 @@ def test_decode_long_single_pass_and_boosted_rows():
     dv.run_decode(d, out)
     out2 = _out(w)
     dv.run_decode_partitioned(d, out2, 512)
+    out3 = _out(w)
+    dv.run_decode_balanced(d, out3)
     torch.cuda.synchronize()
     check_bf16(dv.bits_of(out), ref, "single pass")
     check_bf16(dv.bits_of(out2), ref, "split-KV")
+    check_bf16(dv.bits_of(out3), ref, "balanced")
 
 
 def test_decode_empty_context_is_zero():
@@ -108,8 +115,10 @@ def test_decode_empty_context_is_zero():
     dv.run_decode(d, out)
     out2 = _out(w)
     dv.run_decode_partitioned(d, out2, 16)
+    out3 = _out(w)
+    dv.run_decode_balanced(d, out3)
     torch.cuda.synchronize()
-    for o in (out, out2):
+    for o in (out, out2, out3):
         b = dv.bits_of(o)
         assert np.all(b[0] == 0)
         assert np.all(np.isfinite(oracle.bf16_bits_to_f64(b[1])))
@@ -172,6 +181,26 @@ def test_full_size_config_sampled(cfg):
     dv.run_decode_partitioned(d, out, P)
     out1 = _out(w)
     dv.run_decode(d, out1)
+    out2 = _out(w)
+    dv.run_decode_balanced(d, out2)
     torch.cuda.synchronize()
     check_bf16(dv.bits_of(out)[sample], ref[sample], f"config {cfg} split-KV")
     check_bf16(dv.bits_of(out1)[sample], ref[sample], f"config {cfg} single pass")
+    check_bf16(dv.bits_of(out2)[sample], ref[sample], f"config {cfg} balanced")
+
+
+def test_balanced_workspace_reuse_and_all_units_written():
+    """Two calls in a row on one workspace (the second with fewer requests);
+    every output row is written (NaN-prefilled outputs come back finite)."""
+    _announce("balanced decode: workspace reuse")
+    w1 = wl.config_workload(2, scale_down=2)
+    w2 = wl.make_workload(name="t", seq_lens=[3000, 17, 1, 900], q_lens=[1] * 4,
+                          num_q_heads=32, num_kv_heads=8, head_dim=128, seed=35,
+                          writes_new_kv=False)
+    d1, d2 = dv.to_device(w1), dv.to_device(w2)
+    ws = dv.decode_workspace(d1)
+    for w, d in ((w1, d1), (w2, d2)):
+        out = _out(w)
+        dv.run_decode_balanced(d, out, ws)
+        torch.cuda.synchronize()
+        check_bf16(dv.bits_of(out), oracle.decode(w), "balanced reuse")
