@@ -8,7 +8,10 @@
 // (m, l, A) state, so S and P never reach HBM (§2.1/§2.2 of the second page).
 // Rows of requests with q_len <= 1 are left to the decode kernel.
 //
-// Work-group: (request, query head, 128-query tile); 4 waves x 32 queries.
+// Work-group: (request, KV head, query tile, head chunk).  Its 4 waves share
+// the staged K / V^T tiles: with group size G >= 4 each wave is one query
+// head of the chunk over 32 queries; with G < 4 the waves cover the G heads
+// times 4/G blocks of 32 queries.  Staging is done once per KV group.
 // Per 64-key tile (4 cache blocks):
 //   S^T[64 keys x 32 queries] = K . Q^T   (v_mfma_f32_32x32x16_bf16; keys on
 //       the M side so each lane owns one query column: the softmax row
@@ -29,7 +32,6 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;        // queries per work-group
 constexpr int kBN = 64;         // keys per tile
 constexpr int kWaves = 4;
 constexpr int kQW = 32;         // queries per wave
@@ -58,30 +60,35 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
   constexpr int DBLK = D / 32;            // 32-row d blocks of O^T
   __shared__ PrefillSmem<D> sm;
 
-  // ---- which (request, head, query tile)
+  // ---- which (request, KV head, query tile, head chunk) and this wave's part
   const int r = blockIdx.y;
   const int Hq = a.num_q_heads;
-  int hid = blockIdx.x % Hq;
-  const int tile = blockIdx.x / Hq;
-  if (Hq % 8 == 0) hid = (hid % 8) * (Hq / 8) + hid / 8;   // a KV group stays on one XCD
-  const int h = hid;
+  const int Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int hpw = G < kWaves ? G : kWaves;                  // heads per work-group
+  const int qbw = kWaves / hpw;                             // 32-query blocks per work-group
+  const int nhc = (G + kWaves - 1) / kWaves;                // head chunks per KV head
+  const int unit = blockIdx.x % (Hkv * nhc);
+  const int tile = blockIdx.x / (Hkv * nhc);
+  const int g = unit / nhc, hc = unit - g * nhc;
   (void)tiles_x;
   const int qlo = a.query_start_loc[r];
   const int q_len = a.query_start_loc[r + 1] - qlo;
   if (q_len <= 1) return;                                   // decode path
-  const int i0 = tile * kBM;
+  const int i0 = tile * kQW * qbw;                          // first query of the tile
   if (i0 >= q_len) return;
   const int seq_len = a.seq_lens[r];
   const int pos0 = seq_len - q_len;                         // position of query 0
-  const int G = Hq / a.num_kv_heads;
-  const int g = h / G;
-  const int Hkv = a.num_kv_heads;
 
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
   const int lq = lane % 32, lh = lane / 32;
+  const int hw = w % hpw, qbl = w / hpw;                    // head and query block of the wave
+  const bool wave_on = (qbl < qbw) && (hc * kWaves + hw < G);
+  const int h = g * G + hc * kWaves + (wave_on ? hw : 0);
+  const int wq0 = i0 + qbl * kQW;                           // first query of the wave
 
   // ---- Q fragments (B operand of S^T = K Q^T): query lq, d = 16k + 8lh .. +8
-  const int qi = i0 + w * kQW + lq;                         // query index in request
+  const int qi = wq0 + lq;                                  // query index in request
   const bool q_ok = qi < q_len;
   uint4 qf[KSTEPS];
   {
@@ -94,9 +101,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
     }
   }
   const int p_q = pos0 + qi;                                // this lane's query position
-  const int wave_pmin = pos0 + i0 + w * kQW;                // first query position of the wave
-  const int wave_pmax = pos0 + min(i0 + (w + 1) * kQW, q_len) - 1;
-  const int kend = pos0 + min(i0 + kBM, q_len);             // keys the work-group needs
+  const int wave_pmin = pos0 + wq0;                         // first query position of the wave
+  const int wave_pmax = wave_on ? pos0 + min(wq0 + kQW, q_len) - 1 : -1;   // -1: no work
+  const int kend = pos0 + min(i0 + kQW * qbw, q_len);       // keys the work-group needs
   const int n_tiles = (kend + kBN - 1) / kBN;
 
   float qk_scale = a.scale * kLog2e;
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
 
   // ---- finalize: l over both lane halves, O = A / l, write bf16 rows
   const float l_tot = l_run + xor_lanes(l_run, 32);
-  if (q_ok) {
+  if (q_ok && wave_on) {
     float inv = 1.f / l_tot;
     if constexpr (FP8) inv *= *a.v_scale;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(qlo + qi) * Hq + h) * D;
@@ -294,8 +301,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_reqs == 0 || a.max_query_len <= 1) return hipSuccess;
-  const int tiles = (a.max_query_len + kBM - 1) / kBM;
-  dim3 grid(tiles * a.num_q_heads, a.num_reqs);
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int hpw = G < kWaves ? G : kWaves;
+  const int qbw = kWaves / hpw;
+  const int nhc = (G + kWaves - 1) / kWaves;
+  const int tiles = (a.max_query_len + kQW * qbw - 1) / (kQW * qbw);
+  dim3 grid(tiles * a.num_kv_heads * nhc, a.num_reqs);
   const bool fp8 = a.cache_dtype != 0;
   if (a.head_dim == 64) {
     if (fp8) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(kWaves * 64), 0, st, a, tiles);
