@@ -11,7 +11,10 @@ uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
 Prints ONE JSON line.  value = algorithmic decode bytes (K and V read once
 per KV head, plus Q, O, block-table entries and seq_lens) per second of
 whole step; the roofline object reports the dominant kernel alone, timed
-with HIP events on the stream it runs on.
+with HIP events on the stream it runs on.  The default run also measures
+the three other workloads (long-context split-KV decode, the mixed
+chunked-prefill batch with the prefill kernel's MFMA utilisation, fp8
+shared-prefix decode with its vector-ALU roofline) under `other_workloads`.
 """
 from __future__ import annotations
 
@@ -27,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+# fp32 vector FMA issued one lane-op per lane per clock (no packed math):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 78.6
 
 DESCR = {
     1: "tiny decode: 4 requests, contexts 1/17/33/100, 4 q / 2 KV heads, head_dim 64, bf16",
@@ -104,6 +110,153 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
                       f"{w.num_reqs} requests, all heads) in {dt:.1f} s, fp64 numpy"}
 
 
+def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int) -> dict:
+    """Run `warmup` untimed then `steps` timed steps of workload `cfg`."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_77_amd as pa
+    from paged_kv_cache_77_amd import device as dv
+    from paged_kv_cache_77_amd import workloads as wl
+
+    w = wl.config_workload(cfg, poison=False)
+    d = dv.to_device(w, "cuda")
+    nbytes = decode_bytes(w)
+    if path == "auto":
+        path = "split" if cfg == 3 else "single"
+    P = partition_size or (w.partition_size if cfg == 3 else 1024)
+    is_prefill = cfg == 4
+    T = w.num_tokens
+    sm = torch.empty((max(T, 1),), dtype=torch.int64, device="cuda")
+    rows = T if is_prefill else w.num_reqs
+    out = torch.empty((rows, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    bufs = dv.partial_buffers(d, P) if (path == "split" and not is_prefill) else None
+    ws = dv.decode_workspace(d) if path == "balanced" else None
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(timed: bool):
+        if w.writes_new_kv:
+            dv.write_new_kv_fused(d, sm[:T])      # slot mapping + scatter, one launch
+        e0 = e1 = None
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        if is_prefill:
+            dv.run_prefill(d, out)
+        elif path == "single":
+            dv.run_decode(d, out)
+        elif path == "balanced":
+            dv.run_decode_balanced(d, out, ws)
+        else:
+            tmp, ml, es = bufs
+            pa.pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
+                                     d.seq_lens, d.max_seq_len, float(w.scale), P, tmp, ml,
+                                     es, d.k_scale, d.v_scale)
+            if timed:
+                e1.record(stream)
+            pa.pa_merge_partitions(out, tmp, ml, es, d.seq_lens, P)
+        if timed:
+            if is_prefill or path in ("single", "balanced"):
+                e1.record(stream)
+            ev.append((e0, e1))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    r = {"cfg": cfg, "w": w, "nbytes": nbytes, "ms_step": ms_step, "kern_ms": kern_ms,
+         "path": "varlen" if is_prefill else path,
+         "partition_size": P if (path == "split" and not is_prefill) else None}
+
+    if is_prefill:
+        # the prefill row alone (q_len > 1), timed with events around its launch
+        i = int(np.argmax(w.q_lens))
+        lo, hi = int(w.query_start_loc[i]), int(w.query_start_loc[i + 1])
+        qsl1 = torch.tensor([0, hi - lo], dtype=torch.int32, device="cuda")
+        args1 = (d.layout, out[lo:hi], d.q[lo:hi], d.k_cache, d.v_cache, qsl1,
+                 d.seq_lens[i:i + 1], d.block_table[i:i + 1], hi - lo, int(w.seq_lens[i]),
+                 float(w.scale), d.k_scale, d.v_scale)
+        for _ in range(3):
+            pa.pa_prefill_varlen(*args1)
+        pe = []
+        for _ in range(max(5, steps // 2)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_prefill_varlen(*args1)
+            e1.record(stream)
+            pe.append((e0, e1))
+        torch.cuda.synchronize()
+        pms = sum(a.elapsed_time(b) for a, b in pe) / len(pe)
+        n, ql = int(w.seq_lens[i]), hi - lo
+        pairs = ql * (n - ql) + ql * (ql + 1) // 2
+        flops = 4 * w.head_dim * w.num_q_heads * pairs
+        tf = flops / (pms * 1e-3) / 1e12
+        r["prefill"] = {"bound": "mfma", "kernel": "prefill_kernel (MFMA 32x32x16 bf16)",
+                        "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_for("config4_prefill"), "kernel_ms": round(pms, 5),
+                        "algorithmic_flops_per_launch": flops, "visible_pairs_per_head": pairs}
+        r["kernel"] = "pa_prefill_varlen (decode rows + prefill rows)"
+        r["kbytes"] = nbytes["total"]
+    elif path == "split":
+        nparts = int(((w.seq_lens + P - 1) // P).sum())
+        r["kernel"] = f"decode_kernel (split-KV, P={P})"
+        r["kbytes"] = nbytes["total"] - nbytes["q_o"] // 2 + \
+            nparts * w.num_q_heads * (w.head_dim + 2) * 4
+    elif path == "balanced":
+        r["kernel"] = "decode_balanced_kernel + balanced_merge_kernel"
+        r["kbytes"] = nbytes["total"]
+    else:
+        r["kernel"] = "decode_kernel (single pass)"
+        r["kbytes"] = nbytes["total"]
+    r["key"] = f"config{cfg}_{r['path']}"
+    if w.cache_dtype == "fp8" and not is_prefill:
+        # fp8 codes are decoded to fp32 in registers, so the kernel's floor is
+        # the vector ALU: per (token, KV head) the method does G*d multiply-adds
+        # for q.k and G*d for p*v (2 flop each)
+        G = w.num_q_heads // w.num_kv_heads
+        flops = 4 * G * w.head_dim * nbytes["tokens"] * w.num_kv_heads
+        tf = flops / (kern_ms * 1e-3) / 1e12
+        r["alu"] = {"bound": "alu", "kernel": r["kernel"], "achieved": round(tf, 2),
+                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_FP32_VALU_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": flops}
+    del d, out, bufs, ws, sm
+    torch.cuda.empty_cache()
+    return r
+
+
+def roofline_of(r) -> dict:
+    achieved = r["kbytes"] / (r["kern_ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": r["kernel"], "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic_for(r["key"]), "kernel_ms": round(r["kern_ms"], 5),
+            "algorithmic_bytes_per_launch": r["kbytes"]}
+
+
+def summary(r) -> dict:
+    """Compact record of one workload's measurement."""
+    nb = r["nbytes"]
+    s = {"workload": DESCR[r["cfg"]], "path": r["path"], "partition_size": r["partition_size"],
+         "ms_per_step": round(r["ms_step"], 5),
+         "GBps": round(nb["total"] / (r["ms_step"] * 1e-3) / 1e9, 2),
+         "kv_tokens_per_s": round(nb["tokens"] / (r["ms_step"] * 1e-3), 1),
+         "roofline": roofline_of(r)}
+    if "prefill" in r:
+        s["prefill_roofline"] = r["prefill"]
+    if "alu" in r:
+        s["alu_roofline"] = r["alu"]
+    return s
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +269,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition size in tokens (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="measure the primary workload only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -125,7 +280,6 @@ def main() -> int:
               "no multi-GPU path.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -141,116 +295,11 @@ def main() -> int:
         return 0
 
     import paged_kv_cache_77_amd as pa
-    from paged_kv_cache_77_amd import device as dv
-    from paged_kv_cache_77_amd import workloads as wl
-
     pa.lib()
-    w = wl.config_workload(args.config, poison=False)
-    d = dv.to_device(w, "cuda")
-    nbytes = decode_bytes(w)
-    if args.path == "auto":
-        args.path = "split" if args.config == 3 else "single"
-    P = args.partition_size or (w.partition_size if args.config == 3 else 1024)
-    is_prefill = args.config == 4
-    T = w.num_tokens
-    sm = torch.empty((max(T, 1),), dtype=torch.int64, device="cuda")
-    if is_prefill:
-        out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-    else:
-        out = torch.empty((w.num_reqs, w.num_q_heads, w.head_dim), dtype=torch.bfloat16,
-                          device="cuda")
-    bufs = dv.partial_buffers(d, P) if not is_prefill else None
-    ws = dv.decode_workspace(d) if args.path == "balanced" else None
-    stream = torch.cuda.current_stream()
-    ev = []
 
-    def step(timed: bool):
-        if w.writes_new_kv:
-            dv.write_new_kv_fused(d, sm[:T])      # slot mapping + scatter, one launch
-        e0 = e1 = None
-        if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        if is_prefill:
-            dv.run_prefill(d, out)
-        elif args.path == "single":
-            dv.run_decode(d, out)
-        elif args.path == "balanced":
-            dv.run_decode_balanced(d, out, ws)
-        else:
-            tmp, ml, es = bufs
-            pa.pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
-                                     d.seq_lens, d.max_seq_len, float(w.scale), P, tmp, ml,
-                                     es, d.k_scale, d.v_scale)
-            if timed:
-                e1.record(stream)
-            pa.pa_merge_partitions(out, tmp, ml, es, d.seq_lens, P)
-        if timed:
-            if is_prefill or args.path in ("single", "balanced"):
-                e1.record(stream)
-            ev.append((e0, e1))
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt * 1e3 / args.steps
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-
-    prefill = None
-    if is_prefill:
-        # the prefill row alone (q_len > 1), timed with events around its launch
-        r = int(np.argmax(w.q_lens))
-        lo, hi = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
-        qsl1 = torch.tensor([0, hi - lo], dtype=torch.int32, device="cuda")
-        args1 = (d.layout, out[lo:hi], d.q[lo:hi], d.k_cache, d.v_cache, qsl1,
-                 d.seq_lens[r:r + 1], d.block_table[r:r + 1], hi - lo, int(w.seq_lens[r]),
-                 float(w.scale), d.k_scale, d.v_scale)
-        for _ in range(3):
-            pa.pa_prefill_varlen(*args1)
-        pe = []
-        for _ in range(max(5, args.steps // 2)):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pa.pa_prefill_varlen(*args1)
-            e1.record(stream)
-            pe.append((e0, e1))
-        torch.cuda.synchronize()
-        pms = sum(a.elapsed_time(b) for a, b in pe) / len(pe)
-        n, ql = int(w.seq_lens[r]), hi - lo
-        pairs = ql * (n - ql) + ql * (ql + 1) // 2
-        flops = 4 * w.head_dim * w.num_q_heads * pairs
-        prefill = {"bound": "mfma", "kernel": "prefill_kernel (MFMA 32x32x16 bf16)",
-                   "achieved": round(flops / (pms * 1e-3) / 1e12, 2),
-                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                   "frac": round(flops / (pms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                   "traffic": traffic_for("config4_prefill"), "kernel_ms": round(pms, 5),
-                   "algorithmic_flops_per_launch": flops, "visible_pairs_per_head": pairs}
-
-    if is_prefill:
-        kernel = "pa_prefill_varlen (decode rows + prefill rows)"
-        kbytes = nbytes["total"]
-    elif args.path == "single":
-        kernel = "decode_kernel (single pass)"
-        kbytes = nbytes["total"]
-    elif args.path == "balanced":
-        kernel = "decode_balanced_kernel + balanced_merge_kernel"
-        kbytes = nbytes["total"]
-    else:
-        kernel = f"decode_kernel (split-KV, P={P})"
-        nparts = int(((w.seq_lens + P - 1) // P).sum())
-        part_bytes = nparts * w.num_q_heads * (w.head_dim + 2) * 4
-        kbytes = nbytes["total"] - nbytes["q_o"] // 2 + part_bytes
-    achieved = kbytes / (kern_ms * 1e-3) / 1e9
-    key = f"config{args.config}_{args.path}"
-    tr = traffic_for(key)
-    value = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    r = measure(args.config, args.path, args.partition_size, args.steps, args.warmup)
+    w, nbytes = r["w"], r["nbytes"]
+    value = nbytes["total"] / (r["ms_step"] * 1e-3) / 1e9
     res = {
         "metric": "paged decode attn HBM GB/s (% of MI355X peak) + attended KV tokens/s",
         "value": round(value, 2),
@@ -258,32 +307,36 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(r["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8" if w.cache_dtype == "fp8" else "bf16",
         "data": "synthetic (seeded PCG64 N(0,1), random block permutation)",
         "config": {"workload": DESCR[args.config], "requests": w.num_reqs,
-                   "kv_tokens": nbytes["tokens"], "path": args.path if not is_prefill else
-                   "varlen", "partition_size": P if (args.path == "split" and not is_prefill)
-                   else None, "parallelism": "none (1 GPU)"},
+                   "kv_tokens": nbytes["tokens"], "path": r["path"],
+                   "partition_size": r["partition_size"], "parallelism": "none (1 GPU)"},
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-        "kv_tokens_per_s": round(nbytes["tokens"] / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(nbytes["tokens"] / (r["ms_step"] * 1e-3), 1),
         "algorithmic_bytes_per_step": nbytes["total"],
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": tr, "kernel_ms": round(kern_ms, 5),
-                     "algorithmic_bytes_per_launch": kbytes},
+        "roofline": roofline_of(r),
         "kernel_sha": kernel_source_sha(),
         "inputs_sha256": w.digest(),
     }
-    if prefill is not None:
-        res["prefill_roofline"] = prefill
+    if "prefill" in r:
+        res["prefill_roofline"] = r["prefill"]
+    if "alu" in r:
+        res["alu_roofline"] = r["alu"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
         res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
+    if not args.no_other_workloads and args.config == 2:
+        other = {}
+        for cfg in (3, 4, 5):
+            o = measure(cfg, "auto", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
+            other[f"config{cfg}"] = summary(o)
+            del o
+        res["other_workloads"] = other
     print(json.dumps(res))
     return 0
 
