@@ -30,7 +30,13 @@ Readings of points the pages leave open:
   * query head h reads K/V head h // G, G = num_q_heads / num_kv_heads;
   * no epsilon in the softmax denominator (the result is exact, P1 §2.2);
   * a request with seq_len == 0 produces an all-zero output row;
-  * a negative slot_mapping entry means "skip this token" (padding).
+  * a negative slot_mapping entry means "skip this token" (padding);
+  * writing into an FP8 cache stores the E4M3FN code nearest to the fp32
+    quotient x / scale (ties to the even code, saturating at ±448, NaN kept
+    as NaN) -- the inverse of the read-side "code value times scale";
+  * the ALiBi term of P1 §3.2.4, slope_h · (t − seq_len + 1) for the decode
+    query, is slope_h · (t − p) for a query at position p in prefill (the
+    same relative distance; the decode query sits at p = seq_len − 1).
 """
 from __future__ import annotations
 
@@ -74,6 +80,51 @@ def cache_values(pool: np.ndarray, cache_dtype: str, scale: float = 1.0) -> np.n
     if cache_dtype == "fp8":
         return fp8_e4m3fn_to_f64(pool) * np.float64(np.float32(scale))
     raise ValueError(cache_dtype)
+
+
+def fp8_e4m3fn_encode(y) -> np.ndarray:
+    """fp32 values -> OCP FP8 E4M3FN codes (uint8).
+
+    The code whose value (fp8_e4m3fn_to_f64) is nearest to y; at a tie the
+    code with the even mantissa (round to nearest even).  |y| >= 448, the
+    largest finite E4M3FN value, saturates to ±448 (the format has no
+    infinity); NaN becomes S.1111.111; the sign of y is kept, zeros
+    included.  Written as a search over the 127 non-negative finite values.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    mags = fp8_e4m3fn_to_f64(np.arange(127))          # codes 0x00..0x7E, increasing
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(mags, np.nan_to_num(a, nan=0.0), side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a >= 448.0, 126, code)
+    code = np.where(np.isnan(y), 127, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8(bits: np.ndarray, scale: float) -> np.ndarray:
+    """bf16 bit patterns -> E4M3FN codes for a cache whose per-tensor scale is
+    ``scale`` (reading: the inverse of the read side's code · scale).  The
+    code is decided from the fp32 quotient x / scale, correctly rounded,
+    which is the precision the writing kernel works in."""
+    x = bf16_bits_to_f64(bits).astype(np.float32)     # exact
+    return fp8_e4m3fn_encode(x / np.float32(scale))
+
+
+def alibi_bias(slope: float, key_pos: np.ndarray, query_pos) -> np.ndarray:
+    """ALiBi term added to the scaled score (P1 §3.2.4: slope times
+    (token index − seq_len + 1) for the decode query, i.e. the signed
+    distance from the query's own position).  ``slope`` is the fp32 value
+    the GPU receives, widened."""
+    return float(np.float32(slope)) * (np.asarray(key_pos, np.float64) -
+                                       np.asarray(query_pos, np.float64))
+
+
+def _slopes(w, alibi_slopes):
+    s = getattr(w, "alibi_slopes", None) if alibi_slopes is None else alibi_slopes
+    return None if s is None else np.asarray(s, dtype=np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -120,20 +171,27 @@ def slot_mapping(block_table: np.ndarray, query_start_loc: np.ndarray,
 
 
 def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
-                      value: np.ndarray, slots: np.ndarray, block_size: int):
-    """Write each new token's K/V rows to its slot (bit copy), returning new
-    pools.  The pool layout is [block][kv_head][offset][dim], so slot s lands
-    at block s // B, offset s % B for every KV head (P3 ``reshape_and_cache``
-    writes new K/V through slot_mapping; P1 §3.1 table: slot_mapping writes,
-    block_table reads)."""
+                      value: np.ndarray, slots: np.ndarray, block_size: int,
+                      cache_dtype: str = "bf16", k_scale: float = 1.0,
+                      v_scale: float = 1.0):
+    """Write each new token's K/V rows to its slot, returning new pools.  The
+    pool layout is [block][kv_head][offset][dim], so slot s lands at block
+    s // B, offset s % B for every KV head (P3 ``reshape_and_cache`` writes
+    new K/V through slot_mapping; P1 §3.1 table: slot_mapping writes,
+    block_table reads).  bf16 caches get a bit copy; FP8 caches get the
+    codes of quantize_fp8 with the pool's scale."""
     kp = k_pool.copy()
     vp = v_pool.copy()
     for j, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if s < 0:
             continue
         blk, off = s // block_size, s % block_size
-        kp[blk, :, off, :] = key[j]
-        vp[blk, :, off, :] = value[j]
+        if cache_dtype == "fp8":
+            kp[blk, :, off, :] = quantize_fp8(key[j], k_scale)
+            vp[blk, :, off, :] = quantize_fp8(value[j], v_scale)
+        else:
+            kp[blk, :, off, :] = key[j]
+            vp[blk, :, off, :] = value[j]
     return kp, vp
 
 
@@ -156,13 +214,17 @@ def kv_head_of(h: int, group_size: int) -> int:
     return h // group_size
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """softmax(q Kᵀ · scale) V for query rows q [n, d] over K, V [t, d]
-    (P1 §2.1: S = QKᵀ, P = softmax(S), O = PV).  fp64.  The row max is
-    subtracted before exponentiating, which leaves softmax unchanged."""
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+           bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """softmax(q Kᵀ · scale + bias) V for query rows q [n, d] over K, V [t, d]
+    (P1 §2.1: S = QKᵀ, P = softmax(S), O = PV; bias: the ALiBi term of
+    P1 §3.2.4, added after scaling).  fp64.  The row max is subtracted before
+    exponentiating, which leaves softmax unchanged."""
     if K.shape[0] == 0:
         return np.zeros((q.shape[0], V.shape[1]))
     s = (q @ K.T) * float(np.float32(scale))
+    if bias is not None:
+        s = s + bias
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     return (p @ V) / p.sum(axis=-1, keepdims=True)
@@ -178,27 +240,31 @@ def _request_kv(w, r: int, k_pool=None, v_pool=None):
 
 
 def decode(w, q: Optional[np.ndarray] = None, k_pool=None, v_pool=None,
-           requests: Optional[Iterable[int]] = None) -> np.ndarray:
+           requests: Optional[Iterable[int]] = None, alibi_slopes=None) -> np.ndarray:
     """Single-query decode for every request: out[r, h] = attention of query
     row r, head h over all seq_len[r] tokens of KV head h // G.
     [R, Hq, d] fp64 (rows not in ``requests`` stay NaN).
 
-    q defaults to the workload's query rows (one per request)."""
+    q defaults to the workload's query rows (one per request); ALiBi slopes
+    (one per query head) default to the workload's, if any."""
     qb = w.q if q is None else q
     R, H, d = w.num_reqs, w.num_q_heads, w.head_dim
     G = w.group_size
+    slopes = _slopes(w, alibi_slopes)
     out = np.full((R, H, d), np.nan)
     for r in (range(R) if requests is None else requests):
         K, V = _request_kv(w, r, k_pool, v_pool)
         qr = bf16_bits_to_f64(qb[r])
+        n = int(w.seq_lens[r])
         for h in range(H):
             g = kv_head_of(h, G)
-            out[r, h] = attend(qr[h][None, :], K[:, g, :], V[:, g, :], w.scale)[0]
+            bias = None if slopes is None else alibi_bias(slopes[h], np.arange(n), n - 1)
+            out[r, h] = attend(qr[h][None, :], K[:, g, :], V[:, g, :], w.scale, bias)[0]
     return out
 
 
 def decode_partitions(w, partition_size: int, q: Optional[np.ndarray] = None,
-                      k_pool=None, v_pool=None, requests=None):
+                      k_pool=None, v_pool=None, requests=None, alibi_slopes=None):
     """Per-partition softmax statistics of decode (P1 §3.2.7 and §3.3: V2
     splits the context into fixed partitions and keeps, per partition, the
     max logit, the exp-sum and the partition's normalised output).
@@ -214,6 +280,7 @@ def decode_partitions(w, partition_size: int, q: Optional[np.ndarray] = None,
     l = np.full((R, H, pmax), np.nan)
     O = np.full((R, H, pmax, d), np.nan)
     sc = float(np.float32(w.scale))
+    slopes = _slopes(w, alibi_slopes)
     for r in (range(R) if requests is None else requests):
         K, V = _request_kv(w, r, k_pool, v_pool)
         qr = bf16_bits_to_f64(qb[r])
@@ -223,6 +290,8 @@ def decode_partitions(w, partition_size: int, q: Optional[np.ndarray] = None,
             for h in range(H):
                 g = kv_head_of(h, G)
                 s = (K[lo:hi, g, :] @ qr[h]) * sc
+                if slopes is not None:
+                    s = s + alibi_bias(slopes[h], np.arange(lo, hi), n - 1)
                 mp = s.max()
                 e = np.exp(s - mp)
                 m[r, h, p] = mp
@@ -274,7 +343,7 @@ def online_softmax_tiles(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: flo
 
 
 def prefill_varlen(w, rows: Optional[Iterable[tuple]] = None, k_pool=None,
-                   v_pool=None) -> np.ndarray:
+                   v_pool=None, alibi_slopes=None) -> np.ndarray:
     """Varlen (chunked) prefill over the paged cache (P2 §11.6: the varlen
     batch is cut by query_start_loc; seq_lens give each request's visible
     K/V length; block_table addresses it).  Query i of request r at
@@ -283,6 +352,7 @@ def prefill_varlen(w, rows: Optional[Iterable[tuple]] = None, k_pool=None,
     Returns out [T, Hq, d] fp64.  ``rows``: optional iterable of (token, head)
     pairs to compute (others stay NaN) for sampled checks at full size."""
     T, H, d, G = w.num_tokens, w.num_q_heads, w.head_dim, w.group_size
+    slopes = _slopes(w, alibi_slopes)
     out = np.full((T, H, d), np.nan)
     want = None
     if rows is not None:
@@ -309,6 +379,8 @@ def prefill_varlen(w, rows: Optional[Iterable[tuple]] = None, k_pool=None,
             qs = qf[sel, h, :]
             s = (qs @ K[:, g, :].T) * float(np.float32(w.scale))  # [k, n]
             p_abs = pos[[toks[i] - lo for i in sel]]
+            if slopes is not None:
+                s = s + alibi_bias(slopes[h], np.arange(n)[None, :], p_abs[:, None])
             visible = np.arange(n)[None, :] <= p_abs[:, None]
             s = np.where(visible, s, -np.inf)
             s = s - s.max(axis=-1, keepdims=True)

@@ -72,6 +72,7 @@ class Workload:
     writes_new_kv: bool
     seed: int
     partition_size: int = 512
+    alibi_slopes: Optional[np.ndarray] = None   # fp32 [Hq] or None
 
     @property
     def num_reqs(self) -> int:
@@ -93,7 +94,7 @@ class Workload:
         """SHA-256 of every input buffer (logged next to results)."""
         out = {}
         for name in ("seq_lens", "q_lens", "query_start_loc", "block_table",
-                     "k_pool", "v_pool", "q", "k_new", "v_new"):
+                     "k_pool", "v_pool", "q", "k_new", "v_new", "alibi_slopes"):
             a = getattr(self, name)
             if a is None:
                 continue
@@ -132,7 +133,8 @@ def make_workload(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
                   bt_extra_cols: int = 0, seed: int = 0,
                   perm_seed: Optional[int] = None, identity_perm: bool = False,
                   poison: bool = True, rng: Optional[np.random.Generator] = None,
-                  partition_size: int = 512, zero_q: bool = False) -> Workload:
+                  partition_size: int = 512, zero_q: bool = False,
+                  alibi: bool = False) -> Workload:
     """Build a workload from explicit lengths.
 
     shared_blocks / share: a prefix group of ``shared_blocks`` physical blocks
@@ -142,6 +144,10 @@ def make_workload(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
     k_boost: (period, factor): K rows at logical positions t with
       t % period == period - 1 are multiplied by ``factor`` (a power of two,
       exact in bf16).
+    alibi: attach per-head ALiBi slopes, the geometric sequence
+      2^(-8(h+1)/Hq) of the ALiBi paper (no draws).
+    fp8 caches with new tokens: the per-tensor scales cover the history and
+      the new tokens (amax / 448), so writes do not saturate.
     """
     B = BLOCK_SIZE
     if rng is None:
@@ -153,8 +159,6 @@ def make_workload(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
     assert num_q_heads % num_kv_heads == 0
     assert np.all(q_lens >= 0) and np.all(seq_lens >= q_lens)
     hist = seq_lens - q_lens if writes_new_kv else seq_lens.copy()
-    if cache_dtype == "fp8":
-        assert not writes_new_kv, "the fp8 write path is not part of these workloads"
     share = np.zeros(R, np.int64) if share is None else np.asarray(share, np.int64)
     assert np.all(share <= shared_blocks)
     assert np.all(share * B <= hist), "shared blocks must hold history only"
@@ -263,8 +267,13 @@ def make_workload(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
     # -- 6. fp8 scales and codes
     k_scale = v_scale = np.float32(1.0)
     if fp8:
-        k_scale = np.float32(np.nanmax(np.abs(k_pool)) / FP8_E4M3_MAX)
-        v_scale = np.float32(np.nanmax(np.abs(v_pool)) / FP8_E4M3_MAX)
+        def amax(pool, new):
+            m = float(np.nanmax(np.abs(pool))) if not np.all(np.isnan(pool)) else 0.0
+            if new is not None and new.size:
+                m = max(m, float(np.abs((new.astype(np.uint32) << 16).view(np.float32)).max()))
+            return np.float32(max(m, 1e-6) / FP8_E4M3_MAX)
+        k_scale = amax(k_pool, k_new)
+        v_scale = amax(v_pool, v_new)
         kc = to_fp8_codes(k_pool, k_scale)
         vc = to_fp8_codes(v_pool, v_scale)
         kdead = np.isnan(k_pool)
@@ -283,7 +292,9 @@ def make_workload(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
         block_table=block_table, num_blocks=NB, k_pool=k_pool, v_pool=v_pool,
         q=q, k_new=k_new, v_new=v_new, scale=np.float32(1.0 / np.sqrt(d)),
         k_scale=k_scale, v_scale=v_scale, writes_new_kv=writes_new_kv,
-        seed=seed, partition_size=partition_size)
+        seed=seed, partition_size=partition_size,
+        alibi_slopes=(np.exp2(-8.0 * np.arange(1, H + 1) / H).astype(np.float32)
+                      if alibi else None))
 
 
 # ---------------------------------------------------------------------------

@@ -41,7 +41,7 @@ def test_interleaved_gqa_map_is_caught(monkeypatch):
 
 def test_missing_score_scale_is_caught(monkeypatch):
     real = po.attend
-    monkeypatch.setattr(po, "attend", lambda q, K, V, s: real(q, K, V, 1.0))
+    monkeypatch.setattr(po, "attend", lambda q, K, V, s, *b: real(q, K, V, 1.0, *b))
     _fails(pins.test_decode_matches_sdpa_contiguous, 4, 2, 64)
 
 
@@ -101,3 +101,55 @@ def test_gather_with_wrong_token_order_is_caught(monkeypatch):
     monkeypatch.setattr(po, "gather_kv", wrong)
     _fails(pins.test_decode_matches_sdpa_contiguous, 4, 2, 64)
     _fails(pins.test_scatter_then_gather_roundtrip)
+
+
+def test_fp8_ties_away_from_zero_is_caught(monkeypatch):
+    real = po.fp8_e4m3fn_encode
+
+    def wrong(y):
+        y = np.asarray(y, np.float64)
+        mags = po.fp8_e4m3fn_to_f64(np.arange(127))
+        a = np.abs(y)
+        hi = np.clip(np.searchsorted(mags, np.nan_to_num(a), side="left"), 0, 126)
+        lo = np.clip(hi - 1, 0, 126)
+        code = np.where(mags[hi] - a <= a - mags[lo], hi, lo)     # ties go up
+        code = np.where(a >= 448, 126, code)
+        return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+    monkeypatch.setattr(po, "fp8_e4m3fn_encode", wrong)
+    _fails(pins.test_fp8_encode_ties_saturation_and_specials)
+    _fails(pins.test_fp8_encode_matches_torch_cast_on_all_bf16_inputs)
+    assert real is not wrong
+
+
+def test_fp8_without_saturation_is_caught(monkeypatch):
+    real = po.fp8_e4m3fn_encode
+
+    def wrong(y):
+        y = np.asarray(y, np.float64)
+        return np.where(np.abs(y) > 448, np.uint8(0x7F), real(y)).astype(np.uint8)
+    monkeypatch.setattr(po, "fp8_e4m3fn_encode", wrong)
+    _fails(pins.test_fp8_encode_ties_saturation_and_specials)
+
+
+def test_alibi_sign_flip_is_caught(monkeypatch):
+    real = po.alibi_bias
+    monkeypatch.setattr(po, "alibi_bias", lambda s, k, q: -real(s, k, q))
+    _fails(pins.test_alibi_decode_closed_form)
+    _fails(pins.test_alibi_prefill_closed_form_per_query_position)
+
+
+def test_alibi_key_offset_instead_of_position_is_caught(monkeypatch):
+    real = po.alibi_bias
+    monkeypatch.setattr(po, "alibi_bias",
+                        lambda s, k, q: real(s, np.asarray(k) % 16, np.asarray(q) % 16))
+    _fails(pins.test_alibi_decode_closed_form)
+
+
+def test_alibi_slope_of_kv_head_is_caught(monkeypatch):
+    real = po._slopes
+
+    def wrong(w, a):
+        s = real(w, a)
+        return None if s is None else s[(np.arange(len(s)) // w.group_size) * w.group_size]
+    monkeypatch.setattr(po, "_slopes", wrong)
+    _fails(pins.test_alibi_decode_closed_form)

@@ -385,3 +385,127 @@ def test_kv_sizes(golden):
         elif row[0] == "blocks":
             _, name, toks, B, nb = row
             assert oracle.blocks_for_tokens(int(toks), int(B)) == int(nb), name
+
+
+# ---------------------------------------------------------------------------
+# fp8 write path: quantisation to E4M3FN
+
+
+def test_fp8_encode_roundtrips_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.fp8_e4m3fn_to_f64(codes)          # 0x80 decodes to -0.0
+    assert np.signbit(vals[codes == 0x80]).all()
+    assert np.array_equal(oracle.fp8_e4m3fn_encode(vals), codes)
+
+
+def test_fp8_encode_matches_torch_cast_on_all_bf16_inputs():
+    """Every bf16 bit pattern, divided by several scales in fp32: where the
+    quotient is finite and within ±448, the oracle's code equals torch's
+    round-to-nearest-even float8_e4m3fn cast (a library routine)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    for scale in (1.0, 0.0371, 2.0 ** -8, 3.0, 2.3 / 448):
+        with np.errstate(over="ignore", invalid="ignore"):
+            y = x / np.float32(scale)
+        ok = np.isfinite(y) & (np.abs(y) <= 448)
+        ref = torch.from_numpy(y[ok]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = oracle.fp8_e4m3fn_encode(y[ok])
+        assert ok.sum() > 30000
+        assert np.array_equal(got, ref), scale
+
+
+def test_fp8_encode_ties_saturation_and_specials():
+    e = lambda v: int(oracle.fp8_e4m3fn_encode(np.array([v], dtype=np.float64))[0])
+    assert e(1.0) == 0x38 and e(-1.0) == 0xB8
+    assert e(1.0625) == 0x38          # tie 1.0 | 1.125 -> even mantissa
+    assert e(1.1875) == 0x3A          # tie 1.125 | 1.25 -> even mantissa
+    assert e(1.5 * 2 ** -9) == 0x02 and e(2.5 * 2 ** -9) == 0x02
+    assert e(0.5 * 2 ** -9) == 0x00 and e(0.51 * 2 ** -9) == 0x01
+    assert e(7.5 * 2 ** -9) == 0x08   # subnormal -> smallest normal
+    assert e(447.0) == 0x7E and e(448.0) == 0x7E and e(460.0) == 0x7E
+    assert e(1e30) == 0x7E and e(float("inf")) == 0x7E and e(float("-inf")) == 0xFE
+    assert e(float("nan")) == 0x7F
+    assert e(-0.0) == 0x80 and e(0.0) == 0x00 and e(-1e-9) == 0x80
+
+
+def test_fp8_scatter_writes_codes_of_the_quotient():
+    w = wl.make_workload(name="t", seq_lens=[3, 20], q_lens=[1, 2], num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, seed=5, cache_dtype="fp8")
+    sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, sm, 16,
+                                      cache_dtype="fp8", k_scale=w.k_scale, v_scale=w.v_scale)
+    for j, s in enumerate(sm):
+        blk, off = s // 16, s % 16
+        xv = oracle.bf16_bits_to_f64(w.k_new[j])
+        back = oracle.fp8_e4m3fn_to_f64(kp[blk, :, off, :]) * float(w.k_scale)
+        # within half a code step (relative 1/16) of the value, never saturated
+        assert np.all(np.abs(back - xv) <= np.abs(xv) / 16 + 2.0 ** -10 * float(w.k_scale))
+        assert np.array_equal(kp[blk, :, off, :],
+                              torch.from_numpy(xv.astype(np.float32) / w.k_scale)
+                              .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    untouched = np.ones(kp.shape[0], bool)
+    untouched[sm // 16] = False
+    assert np.array_equal(kp[untouched], w.k_pool[untouched])
+
+
+# ---------------------------------------------------------------------------
+# ALiBi: closed form of a linear bias
+
+
+def _geometric_mean_position(n, slope):
+    """Σ t e^{slope (t - n + 1)} / Σ e^{slope (t - n + 1)} over t < n, by the
+    geometric-series sums with r = e^{-slope}:  (n-1) - Σ k r^k / Σ r^k."""
+    r = math.exp(-slope)
+    s0 = (1 - r ** n) / (1 - r)
+    s1 = r * (1 - n * r ** (n - 1) + (n - 1) * r ** n) / (1 - r) ** 2
+    return (n - 1) - s1 / s0
+
+
+def _positional_workload(seq_lens, q_lens, slopes, hq=4, hkv=2):
+    """K = 0 everywhere, V[t] = t in every element: with ALiBi the output is
+    the bias-weighted mean position."""
+    w = wl.make_workload(name="t", seq_lens=seq_lens, q_lens=q_lens, num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=64, seed=9, writes_new_kv=False)
+    w.k_pool[:] = 0
+    w.v_pool[:] = 0
+    for r, n in enumerate(w.seq_lens):
+        for t in range(int(n)):
+            blk, off = oracle.logical_to_physical(w.block_table[r], t, 16)
+            w.v_pool[blk, :, off, :] = wl.to_bf16_bits(np.full(64, float(t), np.float32))
+    w.alibi_slopes = np.asarray(slopes, np.float32)
+    return w
+
+
+def test_alibi_decode_closed_form():
+    slopes = [0.5, 0.0625, 2.0 ** -8, 1.0]
+    w = _positional_workload([1, 17, 100, 256], [1] * 4, slopes)   # t exact in bf16
+    out = oracle.decode(w)
+    for r, n in enumerate(w.seq_lens):
+        for h in range(4):
+            exp = _geometric_mean_position(int(n), slopes[h]) if n > 1 else 0.0
+            np.testing.assert_allclose(out[r, h], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_alibi_prefill_closed_form_per_query_position():
+    slopes = [0.25, 0.5, 0.125, 2.0 ** -6]
+    w = _positional_workload([40, 250], [40, 7], slopes)
+    out = oracle.prefill_varlen(w)
+    for r in range(2):
+        lo, hi = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
+        pos = oracle.token_positions(int(w.seq_lens[r]), hi - lo)
+        for j, p in zip(range(lo, hi), pos):
+            for h in range(4):
+                exp = _geometric_mean_position(int(p) + 1, slopes[h]) if p > 0 else 0.0
+                np.testing.assert_allclose(out[j, h], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_alibi_partitions_merge_to_decode():
+    w = wl.make_workload(name="t", seq_lens=[700, 33], q_lens=[1, 1], num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, seed=10, writes_new_kv=False,
+                         alibi=True)
+    m, l, O = oracle.decode_partitions(w, 64)
+    merged = oracle.merge_partitions(m, l, O, (w.seq_lens + 63) // 64)
+    np.testing.assert_allclose(merged, oracle.decode(w), rtol=1e-12, atol=1e-12)
+    zero = oracle.decode(w, alibi_slopes=np.zeros(4, np.float32))
+    w.alibi_slopes = None
+    assert np.array_equal(zero, oracle.decode(w))
