@@ -97,15 +97,22 @@ int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
 /*
  * Scatter new K/V into the cache (P3 PagedAttention.write_to_paged_cache ->
  * reshape_and_cache; P1 §3.1 table: slot_mapping writes the new tokens,
- * block_table reads history).  Copies key[j][g][:] to k_cache slot
- * slot_mapping[j], KV head g (and value likewise) bit for bit.  A negative
- * slot skips token j.  Slots must be distinct.
+ * block_table reads history).  Writes key[j][g][:] to k_cache slot
+ * slot_mapping[j], KV head g (and value likewise).  A negative slot skips
+ * token j.  Slots must be distinct.
  *  key, value : bf16 [num_tokens][num_kv_heads][head_dim], contiguous
- * Only PA_CACHE_BF16 layouts are accepted (quantising writes are not built).
+ *  k_scale, v_scale : device fp32 per-tensor scales; required for
+ *    PA_CACHE_FP8_E4M3 layouts, ignored (may be NULL) for bf16
+ * bf16 caches receive a bit copy.  FP8 caches receive, per element x, the
+ * E4M3FN code nearest to the correctly rounded fp32 quotient x / scale, ties
+ * to the even code, saturating at +-448, NaN kept -- the inverse of the read
+ * side, which takes code value * scale (P1 §3.2.1: FP8 vectors are converted
+ * with the scale; the rounding and saturation are this library's reading).
  */
 int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cache,
                          const void* key, const void* value, int32_t num_tokens,
-                         const int64_t* slot_mapping, void* stream);
+                         const int64_t* slot_mapping, const float* k_scale,
+                         const float* v_scale, void* stream);
 
 /*
  * Slot mapping and scatter fused into one launch (the two steps above,
@@ -114,20 +121,24 @@ int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cach
  * pa_compute_slot_mapping would give it; its key/value rows are copied
  * there bit for bit.  Requests own contiguous, increasing row ranges.
  *  slot_mapping : int64 [num_tokens] output, or NULL when not wanted
- * Only PA_CACHE_BF16 layouts are accepted.
+ *  k_scale, v_scale : as pa_reshape_and_cache (FP8 caches are quantised the
+ *                     same way)
  */
 int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void* v_cache,
                                 const void* key, const void* value, const int32_t* block_table,
                                 int32_t bt_stride, const int32_t* query_start_loc,
                                 const int32_t* seq_lens, int32_t num_reqs, int32_t num_tokens,
-                                int64_t* slot_mapping, void* stream);
+                                int64_t* slot_mapping, const float* k_scale,
+                                const float* v_scale, void* stream);
 
 /*
  * Single-query decode attention (P1 §3.2: block-table walk, QK with GQA,
  * masked tail, softmax, PV; P1 §2.2: exact result via the online-softmax
  * state (m, l, A)).  For request r and query head h (g = h / G):
- *     out[r][h] = softmax_t( scale * <q[r][h], K_r[t][g]> ) . V_r[t][g],
- * t over 0 .. seq_lens[r]-1, K_r/V_r read through block_table row r.
+ *     out[r][h] = softmax_t( scale * <q[r][h], K_r[t][g]> + b_h(t) ) . V_r[t][g],
+ * t over 0 .. seq_lens[r]-1, K_r/V_r read through block_table row r, and
+ * b_h(t) = alibi_slopes[h] * (t - seq_lens[r] + 1) when slopes are given
+ * (the ALiBi term of P1 §3.2.4), else 0.
  * One pass per (request, KV head) -- no temporaries.  seq_lens[r] == 0
  * gives a zero row.
  *  out, q     : bf16 [num_reqs][num_q_heads][head_dim]
@@ -135,12 +146,13 @@ int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void*
  *  scale      : softmax scale, e.g. 1/sqrt(head_dim)
  *  k_scale, v_scale : device fp32 scalars, required for FP8 caches,
  *                     ignored (may be NULL) for bf16
+ *  alibi_slopes : device fp32 [num_q_heads], or NULL for no bias
  */
 int pa_decode(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
               int32_t num_q_heads, const void* k_cache, const void* v_cache,
               const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
               int32_t max_seq_len, float scale, const float* k_scale,
-              const float* v_scale, void* stream);
+              const float* v_scale, const float* alibi_slopes, void* stream);
 
 /*
  * Work-balanced decode: the same result as pa_decode (P1 §2.2, §3.2), with
@@ -162,15 +174,16 @@ int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int
                        int32_t num_q_heads, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                        int32_t max_seq_len, float scale, const float* k_scale,
-                       const float* v_scale, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       const float* v_scale, const float* alibi_slopes, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * Split-KV decode, first stage (P1 §3.2.7 and §3.3, the V2 partitioning).
  * Partition p of request r covers tokens [p*P, min((p+1)*P, seq_len)).
  * For every partition p < ceil(seq_lens[r]/P) and query head h writes
- *     max_logits[i] = max of scale*<q,k> over the partition (natural log units)
- *     exp_sums[i]   = sum of exp(scale*<q,k> - max_logits[i])
+ *     max_logits[i] = max of s_t = scale*<q,k_t> + b_h(t) over the partition
+ *                     (natural log units; b_h as in pa_decode)
+ *     exp_sums[i]   = sum of exp(s_t - max_logits[i])
  *     tmp_out[i][:] = sum of exp(...) * v / exp_sums[i]   (fp32)
  * with i = (r*num_q_heads + h)*max_num_partitions + p (the pages' V2 index).
  * Other entries are not written.
@@ -184,7 +197,8 @@ int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num
                           const int32_t* block_table, int32_t bt_stride,
                           const int32_t* seq_lens, int32_t max_seq_len, float scale,
                           const float* k_scale, const float* v_scale,
-                          int32_t partition_size, int32_t max_num_partitions,
+                          const float* alibi_slopes, int32_t partition_size,
+                          int32_t max_num_partitions,
                           float* tmp_out, float* max_logits, float* exp_sums,
                           void* stream);
 
@@ -204,8 +218,10 @@ int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits
  * Varlen (chunked) prefill over the paged cache (P2 §11.6: query_start_loc
  * as cu_seqlens_q, seq_lens as seqused_k, block_table for the paged K/V).
  * Request r owns query rows query_start_loc[r] .. query_start_loc[r+1]-1;
- * row i of it sits at position seq_lens[r] - q_len + i and attends keys
- * 0 .. that position (causal).  Requests with q_len <= 1 take the decode
+ * row i of it sits at position p = seq_lens[r] - q_len + i and attends keys
+ * 0 .. p (causal).  With alibi_slopes, key t's score for head h gains
+ * alibi_slopes[h] * (t - p) (P1 §3.2.4's decode term, whose query sits at
+ * p = seq_len - 1).  Requests with q_len <= 1 take the decode
  * path (P1 §5.2 split_decodes_and_prefills, threshold 1); q_len == 0 writes
  * nothing.  The K/V of this step's tokens must already be in the cache
  * (pa_reshape_and_cache first).
@@ -218,7 +234,7 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q,
                       const int32_t* seq_lens, const int32_t* block_table,
                       int32_t bt_stride, int32_t num_reqs, int32_t max_query_len,
                       int32_t max_seq_len, float scale, const float* k_scale,
-                      const float* v_scale, void* stream);
+                      const float* v_scale, const float* alibi_slopes, void* stream);
 
 /*
  * Test support: gather the logical K and V of every request through the

@@ -109,8 +109,9 @@ def quantize_fp8(bits: np.ndarray, scale: float) -> np.ndarray:
     ``scale`` (reading: the inverse of the read side's code · scale).  The
     code is decided from the fp32 quotient x / scale, correctly rounded,
     which is the precision the writing kernel works in."""
-    x = bf16_bits_to_f64(bits).astype(np.float32)     # exact
-    return fp8_e4m3fn_encode(x / np.float32(scale))
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        x = bf16_bits_to_f64(bits).astype(np.float32)     # exact
+        return fp8_e4m3fn_encode(x / np.float32(scale))
 
 
 def alibi_bias(slope: float, key_pos: np.ndarray, query_pos) -> np.ndarray:

@@ -75,18 +75,19 @@ def lib() -> ctypes.CDLL:
             "pa_status_string": ([_I], ctypes.c_char_p),
             "pa_kv_cache_bytes": ([lp, ctypes.POINTER(ctypes.c_size_t)], _I),
             "pa_compute_slot_mapping": ([_P, _P, _I, _P, _P, _I, _I, _I, _P], _I),
-            "pa_reshape_and_cache": ([lp, _P, _P, _P, _P, _I, _P, _P], _I),
+            "pa_reshape_and_cache": ([lp, _P, _P, _P, _P, _I, _P, _P, _P, _P], _I),
             "pa_reshape_and_cache_varlen": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P,
-                                             _P], _I),
-            "pa_decode": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P], _I),
+                                             _P, _P, _P], _I),
+            "pa_decode": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P, _P],
+                          _I),
             "pa_decode_workspace_size": ([lp, _I, _I], ctypes.c_size_t),
             "pa_decode_balanced": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
-                                    ctypes.c_size_t, _P], _I),
-            "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
+                                    _P, ctypes.c_size_t, _P], _I),
+            "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
                                        _I, _I, _P, _P, _P, _P], _I),
             "pa_merge_partitions": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
             "pa_prefill_varlen": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                   _F, _P, _P, _P], _I),
+                                   _F, _P, _P, _P, _P], _I),
             "pa_debug_gather_kv": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P], _I),
             "pa_debug_fp8_to_f32": ([_P, _P, _I, _P], _I),
             "pa_validate_metadata": ([_P, _I, _P, _P, _I, _P, _I, _I, _I], _I),
@@ -143,30 +144,35 @@ def pa_compute_slot_mapping(slot_mapping, block_table, query_start_loc, seq_lens
         _stream()), "pa_compute_slot_mapping")
 
 
-def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping) -> None:
+def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping, k_scale=None,
+                         v_scale=None) -> None:
     _check(lib().pa_reshape_and_cache(
         ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(key, "key"), _dev(value, "value"), key.shape[0],
-        _dev(slot_mapping, "slot_mapping"), _stream()), "pa_reshape_and_cache")
+        _dev(slot_mapping, "slot_mapping"), _dev(k_scale, "k_scale"),
+        _dev(v_scale, "v_scale"), _stream()), "pa_reshape_and_cache")
 
 
 def pa_reshape_and_cache_varlen(layout, k_cache, v_cache, key, value, block_table,
-                                query_start_loc, seq_lens, slot_mapping=None) -> None:
+                                query_start_loc, seq_lens, slot_mapping=None, k_scale=None,
+                                v_scale=None) -> None:
     _check(lib().pa_reshape_and_cache_varlen(
         ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(key, "key"), _dev(value, "value"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(query_start_loc, "query_start_loc"),
         _dev(seq_lens, "seq_lens"), seq_lens.shape[0], key.shape[0],
-        _dev(slot_mapping, "slot_mapping"), _stream()), "pa_reshape_and_cache_varlen")
+        _dev(slot_mapping, "slot_mapping"), _dev(k_scale, "k_scale"),
+        _dev(v_scale, "v_scale"), _stream()), "pa_reshape_and_cache_varlen")
 
 
 def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
-              scale: float, k_scale=None, v_scale=None) -> None:
+              scale: float, k_scale=None, v_scale=None, alibi_slopes=None) -> None:
     _check(lib().pa_decode(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
-        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()), "pa_decode")
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+        _dev(alibi_slopes, "alibi_slopes"), _stream()), "pa_decode")
 
 
 def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:
@@ -176,23 +182,26 @@ def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:
 
 def pa_decode_balanced(layout, out, q, k_cache, v_cache, block_table, seq_lens,
                        max_seq_len: int, scale: float, workspace, k_scale=None,
-                       v_scale=None) -> None:
+                       v_scale=None, alibi_slopes=None) -> None:
     _check(lib().pa_decode_balanced(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
-        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(workspace, "workspace"),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+        _dev(alibi_slopes, "alibi_slopes"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()), "pa_decode_balanced")
 
 
 def pa_decode_partitioned(layout, q, k_cache, v_cache, block_table, seq_lens,
                           max_seq_len: int, scale: float, partition_size: int, tmp_out,
-                          max_logits, exp_sums, k_scale=None, v_scale=None) -> None:
+                          max_logits, exp_sums, k_scale=None, v_scale=None,
+                          alibi_slopes=None) -> None:
     _check(lib().pa_decode_partitioned(
         ctypes.byref(layout), _dev(q, "q"), q.shape[0], q.shape[1], _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_table, "block_table"), block_table.shape[1],
         _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale), _dev(k_scale, "k_scale"),
-        _dev(v_scale, "v_scale"), int(partition_size), max_logits.shape[2],
+        _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"), int(partition_size),
+        max_logits.shape[2],
         _dev(tmp_out, "tmp_out"), _dev(max_logits, "max_logits"), _dev(exp_sums, "exp_sums"),
         _stream()), "pa_decode_partitioned")
 
@@ -208,14 +217,15 @@ def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,
 
 def pa_prefill_varlen(layout, out, q, k_cache, v_cache, query_start_loc, seq_lens,
                       block_table, max_query_len: int, max_seq_len: int, scale: float,
-                      k_scale=None, v_scale=None) -> None:
+                      k_scale=None, v_scale=None, alibi_slopes=None) -> None:
     _check(lib().pa_prefill_varlen(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
         _dev(block_table, "block_table"), block_table.shape[1], seq_lens.shape[0],
         int(max_query_len), int(max_seq_len), float(scale), _dev(k_scale, "k_scale"),
-        _dev(v_scale, "v_scale"), _stream()), "pa_prefill_varlen")
+        _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"), _stream()),
+        "pa_prefill_varlen")
 
 
 def pa_debug_gather_kv(layout, k_out, v_out, k_cache, v_cache, block_table, seq_lens,

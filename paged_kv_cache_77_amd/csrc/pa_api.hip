@@ -84,26 +84,29 @@ int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
 
 int pa_reshape_and_cache(const pa_kv_layout* layout, void* k_cache, void* v_cache,
                          const void* key, const void* value, int32_t num_tokens,
-                         const int64_t* slot_mapping, void* stream) {
+                         const int64_t* slot_mapping, const float* k_scale,
+                         const float* v_scale, void* stream) {
   PA_TRY(check_layout(layout));
-  if (layout->cache_dtype != PA_CACHE_BF16) return PA_ERR_UNSUPPORTED;
+  PA_TRY(check_scales(layout, 1.f, k_scale, v_scale));
   if (num_tokens < 0) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   if (!k_cache || !v_cache || !key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(key) || !aligned16(value))
     return PA_ERR_INVALID_ARG;
-  return hip_status(pa::launch_reshape_and_cache(k_cache, v_cache, key, value, num_tokens,
-                                                 slot_mapping, layout->num_kv_heads,
-                                                 layout->head_dim, (hipStream_t)stream));
+  return hip_status(pa::launch_reshape_and_cache(
+      k_cache, v_cache, key, value, num_tokens, slot_mapping, layout->num_kv_heads,
+      layout->head_dim, layout->cache_dtype == PA_CACHE_FP8_E4M3, k_scale, v_scale,
+      (hipStream_t)stream));
 }
 
 int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void* v_cache,
                                 const void* key, const void* value, const int32_t* block_table,
                                 int32_t bt_stride, const int32_t* query_start_loc,
                                 const int32_t* seq_lens, int32_t num_reqs, int32_t num_tokens,
-                                int64_t* slot_mapping, void* stream) {
+                                int64_t* slot_mapping, const float* k_scale,
+                                const float* v_scale, void* stream) {
   PA_TRY(check_layout(layout));
-  if (layout->cache_dtype != PA_CACHE_BF16) return PA_ERR_UNSUPPORTED;
+  PA_TRY(check_scales(layout, 1.f, k_scale, v_scale));
   if (num_tokens < 0 || num_reqs < 0 || bt_stride <= 0) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0 || num_reqs == 0) return PA_OK;
   if (!k_cache || !v_cache || !key || !value || !block_table || !query_start_loc || !seq_lens)
@@ -112,7 +115,8 @@ int pa_reshape_and_cache_varlen(const pa_kv_layout* layout, void* k_cache, void*
     return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_reshape_and_cache_varlen(
       k_cache, v_cache, key, value, block_table, bt_stride, query_start_loc, seq_lens, num_reqs,
-      num_tokens, layout->num_kv_heads, layout->head_dim, slot_mapping, (hipStream_t)stream));
+      num_tokens, layout->num_kv_heads, layout->head_dim, slot_mapping,
+      layout->cache_dtype == PA_CACHE_FP8_E4M3, k_scale, v_scale, (hipStream_t)stream));
 }
 
 static int decode_common(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
@@ -136,7 +140,7 @@ static pa::DecodeArgs decode_args(const pa_kv_layout* layout, const void* q, int
                                   const void* v_cache, const int32_t* block_table,
                                   int32_t bt_stride, const int32_t* seq_lens,
                                   int32_t max_seq_len, float scale, const float* k_scale,
-                                  const float* v_scale) {
+                                  const float* v_scale, const float* alibi_slopes) {
   pa::DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -147,6 +151,7 @@ static pa::DecodeArgs decode_args(const pa_kv_layout* layout, const void* q, int
   a.query_start_loc = nullptr;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.alibi_slopes = alibi_slopes;
   a.num_reqs = num_reqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = layout->num_kv_heads;
@@ -162,14 +167,14 @@ int pa_decode(const pa_kv_layout* layout, void* out, const void* q, int32_t num_
               int32_t num_q_heads, const void* k_cache, const void* v_cache,
               const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
               int32_t max_seq_len, float scale, const float* k_scale, const float* v_scale,
-              void* stream) {
+              const float* alibi_slopes, void* stream) {
   PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
                        bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
   if (num_reqs == 0) return PA_OK;
   if (!out || !aligned16(out)) return PA_ERR_INVALID_ARG;
   pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
                                  block_table, bt_stride, seq_lens, max_seq_len, scale,
-                                 k_scale, v_scale);
+                                 k_scale, v_scale, alibi_slopes);
   a.out = out;
   return hip_status(pa::launch_decode(a, false, (hipStream_t)stream));
 }
@@ -186,8 +191,8 @@ int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int
                        int32_t num_q_heads, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                        int32_t max_seq_len, float scale, const float* k_scale,
-                       const float* v_scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       const float* v_scale, const float* alibi_slopes, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
                        bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
   if (num_reqs == 0) return PA_OK;
@@ -198,7 +203,7 @@ int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int
     return PA_ERR_INVALID_ARG;
   pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
                                  block_table, bt_stride, seq_lens, max_seq_len, scale,
-                                 k_scale, v_scale);
+                                 k_scale, v_scale, alibi_slopes);
   a.out = out;
   return hip_status(pa::launch_decode_balanced(a, workspace, (hipStream_t)stream));
 }
@@ -207,7 +212,8 @@ int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num
                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int32_t bt_stride,
                           const int32_t* seq_lens, int32_t max_seq_len, float scale,
-                          const float* k_scale, const float* v_scale, int32_t partition_size,
+                          const float* k_scale, const float* v_scale,
+                          const float* alibi_slopes, int32_t partition_size,
                           int32_t max_num_partitions, float* tmp_out, float* max_logits,
                           float* exp_sums, void* stream) {
   PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
@@ -220,7 +226,7 @@ int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num
   if (!tmp_out || !max_logits || !exp_sums || !aligned16(tmp_out)) return PA_ERR_INVALID_ARG;
   pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
                                  block_table, bt_stride, seq_lens, max_seq_len, scale,
-                                 k_scale, v_scale);
+                                 k_scale, v_scale, alibi_slopes);
   a.tmp_out = tmp_out;
   a.max_logits = max_logits;
   a.exp_sums = exp_sums;
@@ -248,7 +254,8 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
                       const int32_t* query_start_loc, const int32_t* seq_lens,
                       const int32_t* block_table, int32_t bt_stride, int32_t num_reqs,
                       int32_t max_query_len, int32_t max_seq_len, float scale,
-                      const float* k_scale, const float* v_scale, void* stream) {
+                      const float* k_scale, const float* v_scale, const float* alibi_slopes,
+                      void* stream) {
   PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
                        bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
   if (num_tokens < 0 || max_query_len < 0 || max_query_len > max_seq_len)
@@ -259,7 +266,7 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
   // decode-like rows (q_len == 1): the decode kernel, one pass per KV head
   pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
                                  block_table, bt_stride, seq_lens, max_seq_len, scale,
-                                 k_scale, v_scale);
+                                 k_scale, v_scale, alibi_slopes);
   a.out = out;
   a.query_start_loc = query_start_loc;
   PA_TRY(hip_status(pa::launch_decode(a, false, st)));
@@ -274,6 +281,7 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
   p.block_table = block_table;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.alibi_slopes = alibi_slopes;
   p.out = out;
   p.num_reqs = num_reqs;
   p.num_q_heads = num_q_heads;

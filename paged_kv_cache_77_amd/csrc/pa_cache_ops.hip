@@ -2,7 +2,10 @@
 //   slot mapping  -- "vLLM 深度解析（二）：PagedAttention 核心机制" §3.1
 //                    (slot = physical_block * B + offset); "vllm 深度解析：
 //                    一切从 PagedAttention 谈起" (_compute_slot_mappings_kernel)
-//   scatter       -- same page 3: write_to_paged_cache / reshape_and_cache
+//   scatter       -- same page 3: write_to_paged_cache / reshape_and_cache;
+//                    FP8 caches store the E4M3FN code of x / scale (the
+//                    inverse of the read side's code * scale, §3.2.1 of the
+//                    first page)
 //   debug gather  -- the read addressing of §3.1, exposed for bit-exact tests
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -37,14 +40,35 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
   return hipGetLastError();
 }
 
-// One thread per 16-byte chunk of a (token, KV head) row, K and V together.
-// Rows are head_dim bf16 = 8 or 16 chunks; a tile row in the pool is the same
-// head_dim contiguous elements, so the copy is chunk for chunk.
+// Store 8 source elements (one 16-byte chunk of bf16) at chunk index `dst`
+// of the pool: a bit copy for bf16 pools, 8 quantised codes for FP8 pools.
+template <bool FP8>
+__device__ __forceinline__ void store_chunk(void* pool, int64_t dst, const uint4& src,
+                                            float scale) {
+  if constexpr (!FP8) {
+    reinterpret_cast<uint4*>(pool)[dst] = src;
+  } else {
+    const uint32_t w[4] = {src.x, src.y, src.z, src.w};
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? bf16hi(w[e / 2]) : bf16lo(w[e / 2]);
+      c[e / 4] |= f32_to_fp8_e4m3fn(div_rn(x, scale)) << (8 * (e % 4));
+    }
+    reinterpret_cast<uint2*>(pool)[dst] = make_uint2(c[0], c[1]);
+  }
+}
+
+// One thread per 16-byte chunk of a (token, KV head) source row, K and V
+// together.  Rows are head_dim bf16 = 8 or 16 chunks; a tile row in the pool
+// holds the same head_dim elements in order, so chunk c of the source lands
+// at chunk c of the pool row (16 bytes for bf16, 8 codes for FP8).
+template <bool FP8>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    void* __restrict__ k_cache, void* __restrict__ v_cache,
     const uint4* __restrict__ key, const uint4* __restrict__ value,
     const int64_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-    int32_t head_dim) {
+    int32_t head_dim, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   const int chunks = head_dim / 8;                     // 16-byte chunks per row
   const int64_t per_token = (int64_t)num_kv_heads * chunks;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -56,20 +80,27 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t slot = slot_mapping[j];
   if (slot < 0) return;                                // padding token
   const int64_t dst = slot_offset(slot, g, num_kv_heads, head_dim) / 8 + c;
-  k_cache[dst] = key[i];
-  v_cache[dst] = value[i];
+  const float ks = FP8 ? *k_scale : 1.f, vs = FP8 ? *v_scale : 1.f;
+  store_chunk<FP8>(k_cache, dst, key[i], ks);
+  store_chunk<FP8>(v_cache, dst, value[i], vs);
 }
 
 hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key,
                                     const void* value, int32_t num_tokens,
                                     const int64_t* slot_mapping, int32_t num_kv_heads,
-                                    int32_t head_dim, hipStream_t stream) {
+                                    int32_t head_dim, bool fp8, const float* k_scale,
+                                    const float* v_scale, hipStream_t stream) {
   const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     (uint4*)k_cache, (uint4*)v_cache, (const uint4*)key,
-                     (const uint4*)value, slot_mapping, num_tokens, num_kv_heads, head_dim);
+  if (fp8)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0,
+                       stream, k_cache, v_cache, (const uint4*)key, (const uint4*)value,
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0,
+                       stream, k_cache, v_cache, (const uint4*)key, (const uint4*)value,
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, k_scale, v_scale);
   return hipGetLastError();
 }
 
@@ -79,12 +110,14 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* ke
 // in LDS when it fits.
 constexpr int kQslLds = 2048;
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void reshape_and_cache_varlen_kernel(
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ key,
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const uint4* __restrict__ key,
     const uint4* __restrict__ value, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ seq_lens,
     int32_t num_reqs, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-    int64_t* __restrict__ slot_mapping) {
+    int64_t* __restrict__ slot_mapping, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
   __shared__ int32_t qsl[kQslLds];
   const bool in_lds = num_reqs + 1 <= kQslLds;
   if (in_lds) {
@@ -115,8 +148,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_varlen_kernel(
   const int g = rem / chunks;
   const int c = rem - g * chunks;
   const int64_t dst = slot_offset(slot, g, num_kv_heads, head_dim) / 8 + c;
-  k_cache[dst] = key[i];
-  v_cache[dst] = value[i];
+  const float ks = FP8 ? *k_scale : 1.f, vs = FP8 ? *v_scale : 1.f;
+  store_chunk<FP8>(k_cache, dst, key[i], ks);
+  store_chunk<FP8>(v_cache, dst, value[i], vs);
 }
 
 hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const void* key,
@@ -124,15 +158,22 @@ hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const v
                                            int32_t bt_stride, const int32_t* query_start_loc,
                                            const int32_t* seq_lens, int32_t num_reqs,
                                            int32_t num_tokens, int32_t num_kv_heads,
-                                           int32_t head_dim, int64_t* slot_mapping,
+                                           int32_t head_dim, int64_t* slot_mapping, bool fp8,
+                                           const float* k_scale, const float* v_scale,
                                            hipStream_t stream) {
   const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
   if (total == 0 || num_reqs == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(reshape_and_cache_varlen_kernel, dim3((uint32_t)blocks), dim3(256), 0,
-                     stream, (uint4*)k_cache, (uint4*)v_cache, (const uint4*)key,
-                     (const uint4*)value, block_table, bt_stride, query_start_loc, seq_lens,
-                     num_reqs, num_tokens, num_kv_heads, head_dim, slot_mapping);
+  if (fp8)
+    hipLaunchKernelGGL(reshape_and_cache_varlen_kernel<true>, dim3((uint32_t)blocks), dim3(256),
+                       0, stream, k_cache, v_cache, (const uint4*)key, (const uint4*)value,
+                       block_table, bt_stride, query_start_loc, seq_lens, num_reqs, num_tokens,
+                       num_kv_heads, head_dim, slot_mapping, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_varlen_kernel<false>, dim3((uint32_t)blocks), dim3(256),
+                       0, stream, k_cache, v_cache, (const uint4*)key, (const uint4*)value,
+                       block_table, bt_stride, query_start_loc, seq_lens, num_reqs, num_tokens,
+                       num_kv_heads, head_dim, slot_mapping, k_scale, v_scale);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // What is computed ("vLLM 深度解析（二）：PagedAttention 核心机制"):
 //   §3.1   block_table[request][t // B] gives the physical block of token t;
 //   §3.2.4 scores scale*<q, k> for the query heads sharing one KV head,
+//          plus the optional ALiBi term slope_h * (t - seq_len + 1),
 //          positions at or past seq_len excluded;
 //   §3.2.8 V rows past the context never contribute (selected away, since
 //          unwritten slots may hold NaN);
@@ -110,17 +111,29 @@ struct WaveDecoder {
   int lane, kc, krow0, vrg, vcol;
   int nh;                        // real heads of the current unit's chunk
   float qk_scale;
+  bool has_alibi;                // uniform: ALiBi slopes given
+  float alibi;                   // slope of head kc, log2 units (0 without ALiBi)
+  int pos_q;                     // position of the query (seq_len - 1)
   uint32_t qreg[GC][QW];
   float m_run, m_true, l_part;   // lazy max (log2 units), exact max, exp-sum: head kc
   float acc[GC][VE];
 
-  __device__ __forceinline__ void init(int lane_, float qk_scale_) {
+  __device__ __forceinline__ void init(int lane_, float qk_scale_, bool has_alibi_) {
     lane = lane_;
     kc = lane % LPR;             // K lane within its row
     krow0 = lane / LPR;          // first K row; rows krow0 + (64/LPR)*i
     vrg = lane / 16;             // V row group; rows vrg + 4*i
     vcol = (lane % 16) * VE;     // first V element of this lane
     qk_scale = qk_scale_;
+    has_alibi = has_alibi_;
+    alibi = 0.f;
+    pos_q = 0;
+  }
+
+  // ALiBi slope of this lane's head (call after load_q) and the query position
+  __device__ __forceinline__ void set_query(const float* slopes, int h0, int seq_len) {
+    pos_q = seq_len - 1;
+    if (has_alibi) alibi = kc < nh ? slopes[h0 + kc] * kLog2e : 0.f;
   }
 
   // q of query row `row_q`, heads h0 .. h0+nh-1, at this lane's K positions
@@ -220,7 +233,9 @@ struct WaveDecoder {
       for (int j = 1; j < GC; ++j) sv = (kc == j) ? s[i][j] : sv;
       const int tok = tok0 + krow0 + (64 / LPR) * i;
       const bool valid = (kc < nh) && (tok < t_end);
-      x[i] = valid ? sv * qk_scale : -INFINITY;
+      float xv = sv * qk_scale;
+      if (has_alibi) xv = fmaf(alibi, (float)(tok - pos_q), xv);
+      x[i] = valid ? xv : -INFINITY;
       m_true = fmaxf(m_true, x[i]);
       any_big |= x[i] > m_run + kTau;
     }
@@ -421,8 +436,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs a, int n_
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
   Dec dec;
-  dec.init(lane, qk_scale);
+  dec.init(lane, qk_scale, a.alibi_slopes != nullptr);
   dec.load_q(reinterpret_cast<const uint16_t*>(a.q), row_q, a.num_q_heads, h0, nh);
+  dec.set_query(a.alibi_slopes, h0, seq_len);
   dec.reset();
 
   const int first_block = t_begin / kBlock;
@@ -580,7 +596,7 @@ __global__ __launch_bounds__(kBalWaves * 64) void decode_balanced_kernel(
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
   Dec dec;
-  dec.init(lane, qk_scale);
+  dec.init(lane, qk_scale, a.alibi_slopes != nullptr);
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
   const float vs = FP8 ? *a.v_scale : 1.f;
@@ -608,6 +624,7 @@ __global__ __launch_bounds__(kBalWaves * 64) void decode_balanced_kernel(
     if (b0 == 0 || x == x_begin) {
       piece_b0 = b0;            // a new unit (or the wave's first piece)
       dec.load_q(reinterpret_cast<const uint16_t*>(a.q), r, a.num_q_heads, h0, nh);
+      dec.set_query(a.alibi_slopes, h0, seq_len);
       dec.reset();
     }
     // at most kBalSegBlocks blocks per pass; the unit continues in the next pass

@@ -58,6 +58,31 @@ __device__ __forceinline__ f32x4_t fp8x4_to_f32(uint32_t w) {
   return f32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
+// fp32 -> OCP E4M3FN code: round to nearest even, |y| >= 448 saturates to
+// +-448 (the format has no infinity), NaN -> S.1111.111, sign kept.  Integer
+// arithmetic on the fp32 bits: normal results round the 23-bit mantissa to 3
+// bits (a carry moves into the exponent); results below 2^-6 are multiples
+// of 2^-9, found by rounding |y| * 512 (exact) to an integer.
+__device__ __forceinline__ uint32_t f32_to_fp8_e4m3fn(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;                   // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;                  // >= 448, inf: saturate
+  if (a >= 0x3c800000u) {                                     // >= 2^-6: normal
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    return sign | (r - (120u << 3));                          // rebias 127 -> 7
+  }
+  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+}
+
+// x / s for fp32 x, s, correctly rounded: the quotient is formed in fp64
+// (IEEE division) and rounded once more to fp32; with 53 >= 2*24 + 2 bits the
+// double rounding cannot change the result.
+__device__ __forceinline__ float div_rn(float x, float s) {
+  return (float)((double)x / (double)s);
+}
+
 // Two floats -> packed bf16 pair (exact for values representable in bf16,
 // such as decoded FP8).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

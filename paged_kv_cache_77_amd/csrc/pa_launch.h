@@ -1,4 +1,4 @@
-// Kernel launchers of libpa (internal; the C ABI in pa_api.cpp validates
+// Kernel launchers of libpa (internal; the C ABI in pa_api.hip validates
 // arguments and calls these).  Each returns a hipError_t from the launch.
 #pragma once
 
@@ -16,6 +16,7 @@ struct DecodeArgs {
   const int32_t* query_start_loc;   // NULL: q/out row r is request r
   const float* k_scale;             // NULL for bf16 caches
   const float* v_scale;
+  const float* alibi_slopes;        // fp32 [num_q_heads] or NULL (no bias)
   void* out;                        // bf16, final output (NULL in partitioned mode)
   float* tmp_out;                   // partitioned mode only
   float* max_logits;
@@ -36,14 +37,16 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
 hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key,
                                     const void* value, int32_t num_tokens,
                                     const int64_t* slot_mapping, int32_t num_kv_heads,
-                                    int32_t head_dim, hipStream_t stream);
+                                    int32_t head_dim, bool fp8, const float* k_scale,
+                                    const float* v_scale, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const void* key,
                                            const void* value, const int32_t* block_table,
                                            int32_t bt_stride, const int32_t* query_start_loc,
                                            const int32_t* seq_lens, int32_t num_reqs,
                                            int32_t num_tokens, int32_t num_kv_heads,
-                                           int32_t head_dim, int64_t* slot_mapping,
+                                           int32_t head_dim, int64_t* slot_mapping, bool fp8,
+                                           const float* k_scale, const float* v_scale,
                                            hipStream_t stream);
 
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
@@ -80,6 +83,7 @@ struct PrefillArgs {
   const int32_t* block_table;
   const float* k_scale;
   const float* v_scale;
+  const float* alibi_slopes;        // fp32 [num_q_heads] or NULL (no bias)
   void* out;
   int32_t num_reqs, num_q_heads, num_kv_heads, head_dim, cache_dtype;
   int32_t bt_stride;

@@ -4,7 +4,9 @@
 // PagedAttention 核心机制" §2 and §5.2): request r owns query rows
 // query_start_loc[r] .. query_start_loc[r+1]-1; row i sits at position
 // seq_len - q_len + i and attends keys 0..position (causal), K/V read through
-// block_table[r][t / 16].  Tiles of keys are folded in with the running
+// block_table[r][t / 16].  With ALiBi slopes the score of key t for the query
+// at position p gains slope_h * (t - p): the decode term of "vLLM 深度解析
+// （二）" §3.2.4, slope_h * (t - seq_len + 1), is this for p = seq_len - 1.  Tiles of keys are folded in with the running
 // (m, l, A) state, so S and P never reach HBM (§2.1/§2.2 of the second page).
 // Rows of requests with q_len <= 1 are left to the decode kernel.
 //
@@ -53,7 +55,7 @@ struct PrefillSmem {
   uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ ((d >> 1) & 7)]
 };
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool ALIBI>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, int tiles_x) {
   constexpr int CH = D / 8;               // 16-byte chunks per bf16 row
   constexpr int KSTEPS = D / 16;          // MFMA k-steps over d
@@ -108,6 +110,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
 
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
+  // With ALiBi the scores are scaled and biased in place (then sc = 1);
+  // otherwise the scale is applied inside the exponent (sc = qk_scale).
+  const float slope = ALIBI ? a.alibi_slopes[h] * kLog2e : 0.f;
+  const float sc = ALIBI ? 1.f : qk_scale;
 
   const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
   constexpr int EB = FP8 ? 1 : 2;
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
   };
 
   // ---- running state of this lane's query (keys split between lane halves);
-  // m_run is in scaled log2 units, scores s are raw dot products.
+  // m_run is in scaled log2 units, scores s are raw dot products (times sc).
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[DBLK];
 #pragma unroll
@@ -221,7 +227,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
           s[b] = mfma32(kf, qf[k], s[b]);
         }
       }
-      // -- causal mask by select (diagonal tiles only), tile max of raw scores
+      // -- ALiBi: s <- s * qk_scale + slope * (t - p_q)
+      if constexpr (ALIBI) {
+        const float bias0 = slope * (float)(k0 + 4 * lh - p_q);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[b][v] = fmaf(s[b][v], qk_scale,
+                           fmaf(slope, (float)(32 * b + 8 * (v / 4) + (v % 4)), bias0));
+      }
+      // -- causal mask by select (diagonal tiles only), tile max
       if (k0 + kBN - 1 > wave_pmin) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[b][v]);
-      tmax = fmaxf(tmax, xor_lanes(tmax, 32)) * qk_scale;
+      tmax = fmaxf(tmax, xor_lanes(tmax, 32)) * sc;
       // -- lazy rescale: move the max only when it grows by more than 2^8.
       // Key 0 is visible to every query, so m_run is finite after tile 0.
       if (tmax > m_run + 8.0f) {
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(fmaf(s[b][8 * sp + e], qk_scale, -m_run));   // -inf -> 0
+            p[e] = fast_exp2(fmaf(s[b][8 * sp + e], sc, -m_run));   // -inf -> 0
             l_run += p[e];
           }
           pf[2 * b + sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
@@ -308,13 +324,23 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int tiles = (a.max_query_len + kQW * qbw - 1) / (kQW * qbw);
   dim3 grid(tiles * a.num_kv_heads * nhc, a.num_reqs);
   const bool fp8 = a.cache_dtype != 0;
+  const bool alibi = a.alibi_slopes != nullptr;
+#define PA_PREFILL(DV, F8, AL) \
+  hipLaunchKernelGGL((prefill_kernel<DV, F8, AL>), grid, dim3(kWaves * 64), 0, st, a, tiles)
   if (a.head_dim == 64) {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(kWaves * 64), 0, st, a, tiles);
-    else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+    if (fp8) {
+      if (alibi) PA_PREFILL(64, true, true); else PA_PREFILL(64, true, false);
+    } else {
+      if (alibi) PA_PREFILL(64, false, true); else PA_PREFILL(64, false, false);
+    }
   } else {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(kWaves * 64), 0, st, a, tiles);
-    else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(kWaves * 64), 0, st, a, tiles);
+    if (fp8) {
+      if (alibi) PA_PREFILL(128, true, true); else PA_PREFILL(128, true, false);
+    } else {
+      if (alibi) PA_PREFILL(128, false, true); else PA_PREFILL(128, false, false);
+    }
   }
+#undef PA_PREFILL
   return hipGetLastError();
 }
 

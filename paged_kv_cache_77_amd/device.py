@@ -40,6 +40,7 @@ class DeviceWorkload:
     query_start_loc: torch.Tensor
     k_scale: Optional[torch.Tensor]
     v_scale: Optional[torch.Tensor]
+    alibi_slopes: Optional[torch.Tensor]
     max_seq_len: int
     max_query_len: int
 
@@ -51,8 +52,8 @@ class DeviceWorkload:
 def to_device(w, device="cuda") -> DeviceWorkload:
     fp8 = w.cache_dtype == "fp8"
     if fp8:
-        kc = torch.from_numpy(w.k_pool).to(device)
-        vc = torch.from_numpy(w.v_pool).to(device)
+        kc = torch.from_numpy(np.ascontiguousarray(w.k_pool)).to(device)
+        vc = torch.from_numpy(np.ascontiguousarray(w.v_pool)).to(device)
         ks = torch.tensor([w.k_scale], dtype=torch.float32, device=device)
         vs = torch.tensor([w.v_scale], dtype=torch.float32, device=device)
     else:
@@ -68,7 +69,11 @@ def to_device(w, device="cuda") -> DeviceWorkload:
         block_table=torch.from_numpy(w.block_table).to(device),
         seq_lens=torch.from_numpy(w.seq_lens).to(device),
         query_start_loc=torch.from_numpy(w.query_start_loc).to(device),
-        k_scale=ks, v_scale=vs, max_seq_len=int(w.seq_lens.max()) if w.num_reqs else 0,
+        k_scale=ks, v_scale=vs,
+        alibi_slopes=(None if getattr(w, "alibi_slopes", None) is None else
+                      torch.from_numpy(np.ascontiguousarray(w.alibi_slopes, np.float32))
+                      .to(device)),
+        max_seq_len=int(w.seq_lens.max()) if w.num_reqs else 0,
         max_query_len=int(w.q_lens.max()) if w.num_reqs else 0)
 
 
@@ -85,18 +90,20 @@ def partial_buffers(d: DeviceWorkload, partition_size: int):
 def write_new_kv(d: DeviceWorkload, slot_mapping: torch.Tensor) -> None:
     """Slot mapping then scatter of this step's new tokens."""
     pa_compute_slot_mapping(slot_mapping, d.block_table, d.query_start_loc, d.seq_lens)
-    pa_reshape_and_cache(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new, slot_mapping)
+    pa_reshape_and_cache(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new, slot_mapping,
+                         d.k_scale, d.v_scale)
 
 
 def write_new_kv_fused(d: DeviceWorkload, slot_mapping: Optional[torch.Tensor] = None) -> None:
     """The same write in one launch (slots derived in the scatter kernel)."""
     pa_reshape_and_cache_varlen(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new,
-                                d.block_table, d.query_start_loc, d.seq_lens, slot_mapping)
+                                d.block_table, d.query_start_loc, d.seq_lens, slot_mapping,
+                                d.k_scale, d.v_scale)
 
 
 def run_decode(d: DeviceWorkload, out: torch.Tensor) -> None:
     pa_decode(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
-              d.max_seq_len, float(d.w.scale), d.k_scale, d.v_scale)
+              d.max_seq_len, float(d.w.scale), d.k_scale, d.v_scale, d.alibi_slopes)
 
 
 def decode_workspace(d: DeviceWorkload) -> torch.Tensor:
@@ -107,7 +114,8 @@ def decode_workspace(d: DeviceWorkload) -> torch.Tensor:
 def run_decode_balanced(d: DeviceWorkload, out: torch.Tensor, ws=None) -> torch.Tensor:
     ws = decode_workspace(d) if ws is None else ws
     pa_decode_balanced(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
-                       d.max_seq_len, float(d.w.scale), ws, d.k_scale, d.v_scale)
+                       d.max_seq_len, float(d.w.scale), ws, d.k_scale, d.v_scale,
+                       d.alibi_slopes)
     return ws
 
 
@@ -116,7 +124,7 @@ def run_decode_partitioned(d: DeviceWorkload, out: torch.Tensor, partition_size:
     tmp, ml, es = bufs if bufs is not None else partial_buffers(d, partition_size)
     pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
                           d.max_seq_len, float(d.w.scale), partition_size, tmp, ml, es,
-                          d.k_scale, d.v_scale)
+                          d.k_scale, d.v_scale, d.alibi_slopes)
     pa_merge_partitions(out, tmp, ml, es, d.seq_lens, partition_size)
     return tmp, ml, es
 
@@ -124,4 +132,4 @@ def run_decode_partitioned(d: DeviceWorkload, out: torch.Tensor, partition_size:
 def run_prefill(d: DeviceWorkload, out: torch.Tensor) -> None:
     pa_prefill_varlen(d.layout, out, d.q, d.k_cache, d.v_cache, d.query_start_loc,
                       d.seq_lens, d.block_table, d.max_query_len, d.max_seq_len,
-                      float(d.w.scale), d.k_scale, d.v_scale)
+                      float(d.w.scale), d.k_scale, d.v_scale, d.alibi_slopes)

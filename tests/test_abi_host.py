@@ -57,7 +57,7 @@ def _decode_status(layout, num_q_heads=8, ptr=1024, bt_stride=4, max_seq_len=16,
     p = ctypes.c_void_p(ptr)
     o = p if out is None else ctypes.c_void_p(out)
     return L.pa_decode(ctypes.byref(layout), o, p, 2, num_q_heads, p, p, p, bt_stride, p,
-                       max_seq_len, scale, ks, vs, None)
+                       max_seq_len, scale, ks, vs, None, None)
 
 
 def test_decode_rejects_bad_arguments_without_launch():
@@ -82,25 +82,35 @@ def test_partitioned_rejects_bad_partitioning():
 
     def st(P, pmax, max_seq_len=100):
         return L.pa_decode_partitioned(ctypes.byref(lay), p, 2, 8, p, p, p, 8, p, max_seq_len,
-                                       0.1, None, None, P, pmax, p, p, p, None)
+                                       0.1, None, None, None, P, pmax, p, p, p, None)
     assert st(24, 8) == pa.PA_ERR_INVALID_ARG        # not a multiple of 16
     assert st(16, 6) == pa.PA_ERR_INVALID_ARG        # too few partitions for 100 tokens
     assert st(0, 8) == pa.PA_ERR_INVALID_ARG
 
 
-def test_reshape_rejects_fp8_layout():
+def test_fp8_writes_need_scales():
     L = pa.lib()
     lay = pa.make_layout(10, 2, 128, 1)
     p = ctypes.c_void_p(1024)
-    assert L.pa_reshape_and_cache(ctypes.byref(lay), p, p, p, p, 4, p, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache(ctypes.byref(lay), p, p, p, p, 4, p, None, None,
+                                  None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache(ctypes.byref(lay), p, p, p, p, 4, p, p, None,
+                                  None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache_varlen(ctypes.byref(lay), p, p, p, p, p, 4, p, p, 2, 4,
+                                         None, None, p, None) == pa.PA_ERR_INVALID_ARG
+    # bf16 layouts ignore the scales; a misaligned pool is refused before launch
+    bf = pa.make_layout(10, 2, 128, 0)
+    assert L.pa_reshape_and_cache(ctypes.byref(bf), ctypes.c_void_p(1030), p, p, p, 4, p,
+                                  None, None, None) == pa.PA_ERR_INVALID_ARG
 
 
 def test_zero_work_is_ok_without_launch():
     L = pa.lib()
     lay = pa.make_layout(10, 2, 128, 0)
     assert L.pa_decode(ctypes.byref(lay), None, None, 0, 8, None, None, None, 4, None, 0,
-                       0.1, None, None, None) == 0
-    assert L.pa_reshape_and_cache(ctypes.byref(lay), None, None, None, None, 0, None, None) == 0
+                       0.1, None, None, None, None) == 0
+    assert L.pa_reshape_and_cache(ctypes.byref(lay), None, None, None, None, 0, None, None,
+                                  None, None) == 0
 
 
 def test_validate_metadata():
@@ -136,8 +146,8 @@ def test_balanced_workspace_size_and_checks():
     p = ctypes.c_void_p(1024)
     # workspace too small -> invalid argument, nothing launched
     assert L.pa_decode_balanced(ctypes.byref(lay), p, p, 64, 32, p, p, p, 256, p, 4096, 0.1,
-                                None, None, p, n - 16, None) == pa.PA_ERR_INVALID_ARG
+                                None, None, None, p, n - 16, None) == pa.PA_ERR_INVALID_ARG
     # too many requests for the balanced schedule
     big = pa.pa_decode_workspace_size(lay, 5000, 32)
     assert L.pa_decode_balanced(ctypes.byref(lay), p, p, 5000, 32, p, p, p, 256, p, 4096, 0.1,
-                                None, None, p, big, None) == pa.PA_ERR_UNSUPPORTED
+                                None, None, None, p, big, None) == pa.PA_ERR_UNSUPPORTED

@@ -113,3 +113,66 @@ def test_fused_write_ragged_with_empty_requests():
     kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
     assert np.array_equal(dv.bits_of(d.k_cache), kp)
     assert np.array_equal(dv.bits_of(d.v_cache), vp)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0371, 2.0 ** -8, 3.0])
+def test_fp8_quantising_scatter_all_bf16_inputs(scale):
+    """All 65,536 bf16 bit patterns (NaN, inf, subnormals, +-0 included) as K
+    and, reversed, as V; written to an fp8 cache through a shuffled slot
+    mapping, by both write entry points: codes bit-exact vs the oracle."""
+    _announce(f"fp8 quantising write, all bf16 inputs, scale {scale}")
+    T, Hkv, D = 512, 1, 128
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, D)
+    vbits = np.ascontiguousarray(bits[::-1])
+    NB = 40
+    rng = np.random.default_rng(5)
+    slots = rng.permutation(NB * 16)[:T].astype(np.int64)
+    lay = pa.make_layout(NB, Hkv, D, pa.PA_CACHE_FP8_E4M3)
+    ks = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([scale * 0.5], dtype=torch.float32, device="cuda")
+    key, value = dv.bf16_tensor(bits, "cuda"), dv.bf16_tensor(vbits, "cuda")
+    fill = np.full((NB, Hkv, 16, D), 0x5A, dtype=np.uint8)
+    kp_ref, vp_ref = oracle.reshape_and_cache(fill, fill, bits, vbits, slots, 16,
+                                              cache_dtype="fp8", k_scale=np.float32(scale),
+                                              v_scale=np.float32(scale * 0.5))
+    kc = torch.from_numpy(fill.copy()).cuda()
+    vc = torch.from_numpy(fill.copy()).cuda()
+    pa.pa_reshape_and_cache(lay, kc, vc, key, value, torch.from_numpy(slots).cuda(), ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), kp_ref)
+    assert np.array_equal(vc.cpu().numpy(), vp_ref)
+    # the fused entry point: one request of 512 tokens over a shuffled table
+    bt = rng.permutation(NB)[None, :].astype(np.int32)
+    qsl = np.array([0, T], np.int32)
+    sl = np.array([T], np.int32)
+    sm_ref = oracle.slot_mapping(bt, qsl, sl, 16)
+    kp2, vp2 = oracle.reshape_and_cache(fill, fill, bits, vbits, sm_ref, 16, cache_dtype="fp8",
+                                        k_scale=np.float32(scale),
+                                        v_scale=np.float32(scale * 0.5))
+    kc2 = torch.from_numpy(fill.copy()).cuda()
+    vc2 = torch.from_numpy(fill.copy()).cuda()
+    pa.pa_reshape_and_cache_varlen(lay, kc2, vc2, key, value, torch.from_numpy(bt).cuda(),
+                                   torch.from_numpy(qsl).cuda(), torch.from_numpy(sl).cuda(),
+                                   None, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc2.cpu().numpy(), kp2)
+    assert np.array_equal(vc2.cpu().numpy(), vp2)
+
+
+def test_fp8_write_config4_scaled_bit_exact():
+    """The mixed-batch write at 1/8 scale into an fp8 cache (2,176/8 tokens,
+    8 KV heads): slot mapping and codes bit-exact."""
+    _announce("fp8 fused write, mixed batch / 8")
+    w0 = wl.config_workload(4, scale_down=8)
+    w = wl.make_workload(name="t", seq_lens=w0.seq_lens, q_lens=w0.q_lens, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, seed=73, cache_dtype="fp8")
+    d = dv.to_device(w)
+    sm = torch.full((w.num_tokens,), -7, dtype=torch.int64, device="cuda")
+    dv.write_new_kv_fused(d, sm)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    assert np.array_equal(sm.cpu().numpy(), ref_sm)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16,
+                                      cache_dtype="fp8", k_scale=w.k_scale, v_scale=w.v_scale)
+    assert np.array_equal(d.k_cache.cpu().numpy(), kp)
+    assert np.array_equal(d.v_cache.cpu().numpy(), vp)

@@ -204,3 +204,72 @@ def test_balanced_workspace_reuse_and_all_units_written():
         dv.run_decode_balanced(d, out, ws)
         torch.cuda.synchronize()
         check_bf16(dv.bits_of(out), oracle.decode(w), "balanced reuse")
+
+
+@pytest.mark.parametrize("hq,hkv,d,cache", [(32, 8, 128, "bf16"), (28, 4, 128, "fp8"),
+                                            (4, 2, 64, "bf16"), (16, 2, 64, "fp8")])
+def test_decode_alibi_all_paths(hq, hkv, d, cache):
+    """ALiBi slopes 2^(-8(h+1)/Hq): single pass, balanced and split-KV (with
+    the partials) against the oracle."""
+    _announce(f"decode alibi hq={hq} hkv={hkv} d={d} {cache}")
+    w = wl.make_workload(name="t", seq_lens=CTX, q_lens=[1] * len(CTX), num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, seed=70 + hq + d, cache_dtype=cache,
+                         writes_new_kv=False, alibi=True)
+    dd = dv.to_device(w)
+    ref = oracle.decode(w)
+    out = _out(w)
+    dv.run_decode(dd, out)
+    outb = _out(w)
+    dv.run_decode_balanced(dd, outb)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(out), ref, "alibi single")
+    check_bf16(dv.bits_of(outb), ref, "alibi balanced")
+    for P in (64, 512):
+        out2 = _out(w)
+        tmp, ml, es = dv.run_decode_partitioned(dd, out2, P)
+        torch.cuda.synchronize()
+        check_bf16(dv.bits_of(out2), ref, f"alibi partitioned P={P}")
+    m, l, O = oracle.decode_partitions(w, 512)
+    nparts = (w.seq_lens + 511) // 512
+    gm, gl, gO = ml.cpu().numpy(), es.cpu().numpy(), tmp.cpu().numpy()
+    for r in range(w.num_reqs):
+        n = nparts[r]
+        np.testing.assert_allclose(gm[r, :, :n], m[r, :, :n], atol=1e-3, rtol=1e-6)
+        np.testing.assert_allclose(gl[r, :, :n], l[r, :, :n], rtol=1e-3)
+        np.testing.assert_allclose(gO[r, :, :n], O[r, :, :n], atol=2e-3, rtol=0)
+
+
+def test_decode_alibi_zero_slopes_bitwise_equal_plain():
+    """Slopes of 0 give bit-identical outputs to no slopes (the bias is an
+    exact +0)."""
+    _announce("decode alibi zero slopes")
+    w = wl.make_workload(name="t", seq_lens=[77, 1500, 16], q_lens=[1] * 3, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, seed=71, writes_new_kv=False)
+    d = dv.to_device(w)
+    o1, o2 = _out(w), _out(w)
+    dv.run_decode(d, o1)
+    d.alibi_slopes = torch.zeros(32, dtype=torch.float32, device="cuda")
+    dv.run_decode(d, o2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dv.bits_of(o1), dv.bits_of(o2))
+
+
+def test_fp8_decode_after_quantising_write():
+    """fp8 cache lifecycle: new tokens quantised into the cache (fused write),
+    then decode over it; pools bit-exact, outputs within tolerance."""
+    _announce("fp8 write + decode")
+    w = wl.make_workload(name="t", seq_lens=[1, 17, 300, 2049, 64], q_lens=[1] * 5,
+                         num_q_heads=28, num_kv_heads=4, head_dim=128, seed=72,
+                         cache_dtype="fp8", bt_extra_cols=2)
+    d = dv.to_device(w)
+    dv.write_new_kv_fused(d, None)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16,
+                                      cache_dtype="fp8", k_scale=w.k_scale, v_scale=w.v_scale)
+    assert np.array_equal(d.k_cache.cpu().numpy(), kp)
+    assert np.array_equal(d.v_cache.cpu().numpy(), vp)
+    out = _out(w)
+    dv.run_decode(d, out)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(out), oracle.decode(w, k_pool=kp, v_pool=vp), "fp8 write + decode")

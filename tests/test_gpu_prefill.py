@@ -24,7 +24,11 @@ def _run(w, write=True):
         sm = torch.empty((w.num_tokens,), dtype=torch.int64, device="cuda")
         dv.write_new_kv(d, sm)
         ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
-        kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
+        kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16,
+                                          cache_dtype=w.cache_dtype, k_scale=w.k_scale,
+                                          v_scale=w.v_scale)
+        assert np.array_equal(dv.bits_of(d.k_cache) if w.cache_dtype == "bf16"
+                              else d.k_cache.cpu().numpy(), kp), "K pool after the write"
     out = torch.full((w.num_tokens, w.num_q_heads, w.head_dim), float("nan"),
                      dtype=torch.bfloat16, device="cuda")
     dv.run_prefill(d, out)
@@ -120,3 +124,25 @@ def test_config4_full_size_sampled():
     rows = [(t, h) for t in toks for h in range(w.num_q_heads)]
     ref = oracle.prefill_varlen(w, rows=rows, k_pool=kp, v_pool=vp)
     check_bf16(got[toks], ref[toks], "config 4 sampled rows")
+
+
+@pytest.mark.parametrize("hq,hkv,d,cache", [(32, 8, 128, "bf16"), (28, 4, 128, "fp8"),
+                                            (4, 2, 64, "bf16")])
+def test_prefill_alibi(hq, hkv, d, cache):
+    """ALiBi slopes (2^(-8(h+1)/Hq)) on the mixed batch: prefill rows take
+    slope * (t - p), the decode rows slope * (t - seq_len + 1)."""
+    _announce(f"prefill alibi hq={hq} hkv={hkv} d={d} {cache}")
+    w = wl.make_workload(name="t", num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                         seed=60 + hq + d, cache_dtype=cache, alibi=True, **MIX)
+    got, kp, vp = _run(w)
+    check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "prefill alibi")
+
+
+def test_prefill_fp8_cache_with_new_tokens():
+    """The whole fp8 step: quantising write of the new tokens, then prefill
+    and decode rows over the fp8 cache."""
+    _announce("prefill fp8 with quantising write")
+    w = wl.make_workload(name="t", num_q_heads=28, num_kv_heads=4, head_dim=128, seed=61,
+                         cache_dtype="fp8", **MIX)
+    got, kp, vp = _run(w)
+    check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "prefill fp8 + write")
