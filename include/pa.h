@@ -256,6 +256,12 @@ int pa_debug_gather_kv(const pa_kv_layout* layout, void* k_out, void* v_out,
 int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
 
 /*
+ * Test support: decode n FP8 E4M3FN codes to f16 bit patterns with the
+ * conversion the decode kernels use for FP8 V rows.
+ */
+int pa_debug_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream);
+
+/*
  * Host-side check of metadata the kernels trust.  All arrays are HOST
  * pointers.  Checks: query_start_loc starts at 0 and is non-decreasing;
  * 0 <= q_len <= seq_len; seq_len <= bt_stride*block_size; every block-table

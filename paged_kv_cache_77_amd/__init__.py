@@ -20,7 +20,8 @@ __all__ = [
     "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
-    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata", "EXPORTED_SYMBOLS",
+    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
+    "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "pa_reshape_and_cache", "pa_reshape_and_cache_varlen", "pa_decode",
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
-    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_validate_metadata",
+    "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
 )
 
 
@@ -90,6 +91,7 @@ def lib() -> ctypes.CDLL:
                                    _F, _P, _P, _P, _P], _I),
             "pa_debug_gather_kv": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P], _I),
             "pa_debug_fp8_to_f32": ([_P, _P, _I, _P], _I),
+            "pa_debug_fp8_to_f16": ([_P, _P, _I, _P], _I),
             "pa_validate_metadata": ([_P, _I, _P, _P, _I, _P, _I, _I, _I], _I),
         }
         for name, (args, res) in sig.items():
@@ -240,6 +242,11 @@ def pa_debug_gather_kv(layout, k_out, v_out, k_cache, v_cache, block_table, seq_
 def pa_debug_fp8_to_f32(codes, out) -> None:
     _check(lib().pa_debug_fp8_to_f32(_dev(codes, "codes"), _dev(out, "out"), codes.numel(),
                                      _stream()), "pa_debug_fp8_to_f32")
+
+
+def pa_debug_fp8_to_f16(codes, out) -> None:
+    _check(lib().pa_debug_fp8_to_f16(_dev(codes, "codes"), _dev(out, "out"), codes.numel(),
+                                     _stream()), "pa_debug_fp8_to_f16")
 
 
 def pa_validate_metadata(block_table, query_start_loc, seq_lens, slot_mapping,

@@ -319,6 +319,13 @@ int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* strea
   return hip_status(pa::launch_fp8_to_f32(codes, out, n, (hipStream_t)stream));
 }
 
+int pa_debug_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream) {
+  if (n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!codes || !out) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_fp8_to_f16(codes, out, n, (hipStream_t)stream));
+}
+
 int pa_validate_metadata(const int32_t* block_table, int32_t bt_stride,
                          const int32_t* query_start_loc, const int32_t* seq_lens,
                          int32_t num_reqs, const int64_t* slot_mapping, int32_t num_tokens,

@@ -240,3 +240,33 @@ hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// Four codes per thread through the FP8 -> f16 pair conversion of the decode
+// kernel's V path (both halves of the word).
+__global__ __launch_bounds__(256) void fp8_to_f16_kernel(const uint8_t* __restrict__ codes,
+                                                         uint16_t* __restrict__ out, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base = i * 4;
+  if (base >= n) return;
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k)
+    if (base + k < n) w |= (uint32_t)codes[base + k] << (8 * k);
+  const uint32_t lo = fp8x2_to_f16x2<false>(w), hi = fp8x2_to_f16x2<true>(w);
+  const uint16_t vals[4] = {(uint16_t)(lo & 0xffffu), (uint16_t)(lo >> 16),
+                            (uint16_t)(hi & 0xffffu), (uint16_t)(hi >> 16)};
+  for (int k = 0; k < 4; ++k)
+    if (base + k < n) out[base + k] = vals[k];
+}
+
+hipError_t launch_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n,
+                             hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int threads = (n + 3) / 4;
+  hipLaunchKernelGGL(fp8_to_f16_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream,
+                     codes, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace pa

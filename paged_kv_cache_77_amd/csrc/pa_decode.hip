@@ -25,7 +25,11 @@
 //      chunk for the softmax (exp, running max, exp-sum).
 //   V: 16 lanes per row, rows rg, rg+4, rg+8, rg+12 (rg = lane/16), each lane
 //      holding D/16 contiguous elements; accumulators acc[head][D/16].
-//   p moves from K lanes to V lanes through a per-wave LDS slab.
+//   p moves from K lanes to V lanes through a per-wave LDS slab.  FP8 caches
+//   take a cheaper PV: each K lane stores its two rows' p (rows r, r + 8) as
+//   one f16 pair, V lanes interleave the codes of rows r and r + 8, convert
+//   them to exact f16 pairs and accumulate with v_dot2_f32_f16 (two tokens
+//   per instruction), halving the vector-ALU work of PV.
 //
 // Online softmax in log2 units (scores pre-multiplied by log2 e) with a lazy
 // running max: the max of head h only moves when a score exceeds it by more
@@ -260,18 +264,74 @@ struct WaveDecoder {
         for (int e = 0; e < VE; ++e) acc[j][e] *= aj;
       }
     }
-    // -- probabilities to the LDS slab
+    // -- probabilities to the LDS slab: fp32 [16 rows][GCP] for bf16 caches;
+    // for FP8 caches one f16 pair per (row pair, head): rows krow0 and
+    // krow0 + 8 (this lane's two K rows) share a word, [8 pairs][GCP].
+    if constexpr (FP8) {
+      static_assert(RK == 2 && 64 / LPR == 8, "row pairs (r, r + 8)");
+      float pr[RK];
 #pragma unroll
-    for (int i = 0; i < RK; ++i) {
-      const float p = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
-      l_part += p;
-      if (kc < GC) slab[(krow0 + (64 / LPR) * i) * GCP + kc] = p;
+      for (int i = 0; i < RK; ++i) {
+        pr[i] = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
+        l_part += pr[i];
+      }
+      if (kc < GC) reinterpret_cast<uint32_t*>(slab)[krow0 * GCP + kc] = pack_f16x2(pr[0], pr[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RK; ++i) {
+        const float p = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
+        l_part += p;
+        if (kc < GC) slab[(krow0 + (64 / LPR) * i) * GCP + kc] = p;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // -- PV: this lane's 4 V rows
     const bool full = tok0 + kBlock <= t_end;
+    if constexpr (FP8) {
+      // Rows (vrg + 4ip, vrg + 4ip + 8) in pairs: their codes are interleaved
+      // byte-wise, converted to f16 pairs (exact) and multiplied with the f16
+      // p pairs by v_dot2_f32_f16, two tokens per instruction.
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        const int ra = vrg + 4 * ip;
+        uint32_t pp[GCP];
+#pragma unroll
+        for (int q4 = 0; q4 < GCP / 4; ++q4) {
+          const uint4 p4 = *reinterpret_cast<const uint4*>(
+              &reinterpret_cast<const uint32_t*>(slab)[ra * GCP + q4 * 4]);
+          pp[q4 * 4 + 0] = p4.x; pp[q4 * 4 + 1] = p4.y;
+          pp[q4 * 4 + 2] = p4.z; pp[q4 * 4 + 3] = p4.w;
+        }
+        Words<VW> wa = t.v[ip], wb = t.v[ip + 2];
+        if (!full) {
+          if (tok0 + ra >= t_end) {
+#pragma unroll
+            for (int u = 0; u < VW; ++u) wa.w[u] = 0u;     // past the context: exclude
+          }
+          if (tok0 + ra + 8 >= t_end) {
+#pragma unroll
+            for (int u = 0; u < VW; ++u) wb.w[u] = 0u;
+          }
+        }
+        uint32_t hv[VE];                 // f16 pairs (v[ra][e], v[ra + 8][e])
+#pragma unroll
+        for (int u = 0; u < VW; ++u) {
+          const uint32_t x01 = perm_bytes(wb.w[u], wa.w[u], 0x05010400u);   // a0 b0 a1 b1
+          const uint32_t x23 = perm_bytes(wb.w[u], wa.w[u], 0x07030602u);   // a2 b2 a3 b3
+          hv[4 * u + 0] = fp8x2_to_f16x2<false>(x01);
+          hv[4 * u + 1] = fp8x2_to_f16x2<true>(x01);
+          hv[4 * u + 2] = fp8x2_to_f16x2<false>(x23);
+          hv[4 * u + 3] = fp8x2_to_f16x2<true>(x23);
+        }
+#pragma unroll
+        for (int j = 0; j < GC; ++j)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[j][e] = dot2_f16(pp[j], hv[e], acc[j][e]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = vrg + 4 * i;

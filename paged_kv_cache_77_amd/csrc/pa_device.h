@@ -13,6 +13,7 @@ constexpr int kBlock = 16;   // tokens per cache block
 constexpr int kWave = 64;    // CDNA wavefront
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -93,6 +94,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two OCP E4M3FN codes (bytes 0,1 of w when hi is false, bytes 2,3 when
+// true) -> an f16 pair, low half from the lower byte.  Exact: every finite
+// E4M3FN value is an f16 value (scale operand 1.0).
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
+}
+
+// Two floats -> f16 pair (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                c, false);
+}
+
+// Byte shuffle of two words: result byte i = byte sel_i of the 8 bytes
+// {lo[0..3], hi[0..3]} (selector values 0..7).
+__device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
 // ---------------------------------------------------------------------------

@@ -58,6 +58,8 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
 
 hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
                              hipStream_t stream);
+hipError_t launch_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n,
+                             hipStream_t stream);
 
 // Decode: partitioned == false writes args.out directly (one pass per
 // request and KV head); true writes the partials.

@@ -27,6 +27,21 @@ def test_fp8_conversion_all_codes():
     assert np.array_equal(got[ok], ref[ok])
 
 
+def test_fp8_to_f16_conversion_all_codes():
+    """The f16 conversion of the decode kernels' FP8 V path, all 256 codes:
+    exact (every finite E4M3FN value is an f16 value), NaN stays NaN."""
+    _announce("fp8 e4m3fn -> f16, 256 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    out = torch.empty(256, dtype=torch.int16, device="cuda")
+    pa.pa_debug_fp8_to_f16(codes, out)
+    got = out.cpu().numpy().view(np.float16).astype(np.float64)
+    ref = oracle.fp8_e4m3fn_to_f64(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
 def _write_and_check(w):
     d = dv.to_device(w)
     T = w.num_tokens
