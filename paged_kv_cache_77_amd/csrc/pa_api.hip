@@ -289,6 +289,7 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
   p.head_dim = layout->head_dim;
   p.cache_dtype = layout->cache_dtype;
   p.bt_stride = bt_stride;
+  p.num_tokens = num_tokens;
   p.max_query_len = max_query_len;
   p.max_seq_len = max_seq_len;
   p.scale = scale;

@@ -89,6 +89,7 @@ struct PrefillArgs {
   void* out;
   int32_t num_reqs, num_q_heads, num_kv_heads, head_dim, cache_dtype;
   int32_t bt_stride;
+  int32_t num_tokens;               // query rows in the batch
   int32_t max_query_len, max_seq_len;
   float scale;
 };

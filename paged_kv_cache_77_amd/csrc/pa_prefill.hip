@@ -26,6 +26,8 @@
 // (d-major) with the key permutation and a swizzle on d >> 1 (rows of V^T are
 // 128 bytes, so two consecutive rows share a 256-byte bank line); both
 // double-buffered.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -37,6 +39,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kBN = 64;         // keys per tile
 constexpr int kWaves = 4;
 constexpr int kQW = 32;         // queries per wave
+constexpr int kMaxPrefillGroups = 4096;   // work-groups of one launch (a multiple of 8)
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -55,30 +58,32 @@ struct PrefillSmem {
   uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ ((d >> 1) & 7)]
 };
 
+// Work-group shape: hpw heads x qbw 32-query blocks (hpw * qbw == kWaves).
+__host__ __device__ inline void prefill_shape(int G, int& hpw, int& qbw, int& nhc) {
+  hpw = G < kWaves ? G : kWaves;                            // heads per work-group
+  qbw = kWaves / hpw;                                       // 32-query blocks per work-group
+  nhc = (G + kWaves - 1) / kWaves;                          // head chunks per KV head
+}
+
+// One work item: query tile `tile` (kQW * qbw queries) of request r, KV head
+// group `unit` (KV head unit / nhc, head chunk unit % nhc).
 template <int D, bool FP8, bool ALIBI>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, int tiles_x) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D>& sm, int r,
+                                             int tile, int unit) {
   constexpr int CH = D / 8;               // 16-byte chunks per bf16 row
   constexpr int KSTEPS = D / 16;          // MFMA k-steps over d
   constexpr int DBLK = D / 32;            // 32-row d blocks of O^T
-  __shared__ PrefillSmem<D> sm;
 
-  // ---- which (request, KV head, query tile, head chunk) and this wave's part
-  const int r = blockIdx.y;
+  // ---- this wave's part of the item
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  const int hpw = G < kWaves ? G : kWaves;                  // heads per work-group
-  const int qbw = kWaves / hpw;                             // 32-query blocks per work-group
-  const int nhc = (G + kWaves - 1) / kWaves;                // head chunks per KV head
-  const int unit = blockIdx.x % (Hkv * nhc);
-  const int tile = blockIdx.x / (Hkv * nhc);
+  int hpw, qbw, nhc;
+  prefill_shape(G, hpw, qbw, nhc);
   const int g = unit / nhc, hc = unit - g * nhc;
-  (void)tiles_x;
   const int qlo = a.query_start_loc[r];
   const int q_len = a.query_start_loc[r + 1] - qlo;
-  if (q_len <= 1) return;                                   // decode path
   const int i0 = tile * kQW * qbw;                          // first query of the tile
-  if (i0 >= q_len) return;
   const int seq_len = a.seq_lens[r];
   const int pos0 = seq_len - q_len;                         // position of query 0
 
@@ -315,18 +320,100 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a, 
   }
 }
 
+// The work items are the query tiles of the requests with q_len > 1, in
+// request order, times the KV-head groups: item k is flattened tile k / U of
+// KV-head group k % U (U = num_kv_heads * nhc).  Wave 0 of a work-group finds
+// the request holding a flattened tile by a running prefix over the
+// requests' tile counts, 64 requests per step.  Work-groups take items
+// blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized by a bound on
+// the tile count (decode rows cost no work-groups).
+// With direct != 0 (few requests) the grid is (tiles * U, num_reqs) instead:
+// one item per work-group, request blockIdx.y, no search.
+template <int D, bool FP8, bool ALIBI>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
+                                                                 int64_t num_items,
+                                                                 int direct) {
+  __shared__ PrefillSmem<D> sm;
+  __shared__ int sched[2];
+  int hpw, qbw, nhc;
+  prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
+  const int U = a.num_kv_heads * nhc;
+  const int QT = kQW * qbw;
+  if (direct) {
+    const int r = blockIdx.y, tile = blockIdx.x / U;
+    const int q_len = a.query_start_loc[r + 1] - a.query_start_loc[r];
+    if (q_len <= 1 || tile * QT >= q_len) return;
+    prefill_item<D, FP8, ALIBI>(a, sm, r, tile, blockIdx.x % U);
+    return;
+  }
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int64_t k = blockIdx.x; k < num_items; k += gridDim.x) {
+    const int64_t kt = k / U;
+    if (w == 0) {
+      int64_t base = 0;
+      int found_r = -1, found_t = 0;
+      for (int r0 = 0; r0 < a.num_reqs && found_r < 0; r0 += 64) {
+        const int rr = r0 + lane;
+        int nt = 0;
+        if (rr < a.num_reqs) {
+          const int ql = a.query_start_loc[rr + 1] - a.query_start_loc[rr];
+          nt = ql > 1 ? (ql + QT - 1) / QT : 0;
+        }
+        int incl = nt;                                       // inclusive prefix in the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += v;
+        }
+        const int excl = incl - nt;
+        const bool mine = nt > 0 && kt >= base + excl && kt < base + incl;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+        if (m != 0) {
+          const int src = __builtin_ctzll(m);
+          found_r = r0 + src;
+          found_t = (int)(kt - base - __shfl(excl, src, 64));
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) {
+        sched[0] = found_r;
+        sched[1] = found_t;
+      }
+    }
+    __syncthreads();
+    // uniform across the work-group: keep them scalar
+    const int r = __builtin_amdgcn_readfirstlane(sched[0]);
+    const int tile = __builtin_amdgcn_readfirstlane(sched[1]);
+    __syncthreads();
+    if (r < 0) break;                                        // past the last tile
+    prefill_item<D, FP8, ALIBI>(a, sm, r, tile, (int)(k % U));
+    __syncthreads();
+  }
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_reqs == 0 || a.max_query_len <= 1) return hipSuccess;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int hpw = G < kWaves ? G : kWaves;
-  const int qbw = kWaves / hpw;
-  const int nhc = (G + kWaves - 1) / kWaves;
-  const int tiles = (a.max_query_len + kQW * qbw - 1) / (kQW * qbw);
-  dim3 grid(tiles * a.num_kv_heads * nhc, a.num_reqs);
+  int hpw, qbw, nhc;
+  prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
+  const int QT = kQW * qbw;
+  // tiles <= sum over prefill requests of (q_len / QT + 1) <= T / QT + #prefill
+  // requests, with #prefill requests <= min(num_reqs, T / 2) and each tile
+  // count <= ceil(max_query_len / QT)
+  const int64_t T = a.num_tokens;
+  const int64_t per_req = (a.max_query_len + QT - 1) / QT;
+  const int64_t nreq_bound = std::min<int64_t>(a.num_reqs, T / 2);
+  const int64_t tiles = std::min<int64_t>((T + QT - 1) / QT + nreq_bound, per_req * nreq_bound);
+  const int64_t num_items = tiles * a.num_kv_heads * nhc;
+  if (num_items == 0) return hipSuccess;
+  // few requests: the direct grid wastes at most a few work-groups
+  const int direct = a.num_reqs <= 4 ? 1 : 0;
+  dim3 grid((unsigned)std::min<int64_t>(num_items, kMaxPrefillGroups));
+  if (direct) grid = dim3((unsigned)(per_req * a.num_kv_heads * nhc), a.num_reqs);
   const bool fp8 = a.cache_dtype != 0;
   const bool alibi = a.alibi_slopes != nullptr;
 #define PA_PREFILL(DV, F8, AL) \
-  hipLaunchKernelGGL((prefill_kernel<DV, F8, AL>), grid, dim3(kWaves * 64), 0, st, a, tiles)
+  hipLaunchKernelGGL((prefill_kernel<DV, F8, AL>), grid, dim3(kWaves * 64), 0, st, a, num_items, \
+                     direct)
   if (a.head_dim == 64) {
     if (fp8) {
       if (alibi) PA_PREFILL(64, true, true); else PA_PREFILL(64, true, false);
