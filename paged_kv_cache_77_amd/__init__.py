@@ -42,6 +42,11 @@ EXPORTED_SYMBOLS = (
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
+    # host block manager (include/pa_blocks.h; binding in blocks.py)
+    "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
+    "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
+    "pa_pool_free_blocks", "pa_pool_cache_block", "pa_pool_allocate_prompt", "pa_pool_commit",
+    "pa_pool_free_request",
 )
 
 

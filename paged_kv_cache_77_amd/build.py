@@ -1,4 +1,5 @@
-"""Build libpa.so (all HIP sources under csrc/) for gfx950 with hipcc.
+"""Build libpa.so for gfx950: the HIP sources under csrc/ with hipcc, the
+host-only C++ sources (csrc/*.cpp: the block manager) with g++.
 
 Objects go to csrc/../_build/, the library next to this file.  Every call
 recompiles (the build check must exercise the compiler).
@@ -18,6 +19,8 @@ LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept out of generated code
@@ -27,15 +30,20 @@ FLAGS = [
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    stem, ext = os.path.splitext(os.path.basename(src))
+    obj = os.path.join(BUILD, f"{stem}{ext.replace('.', '_')}.o")
+    if ext == ".hip":
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compile failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 

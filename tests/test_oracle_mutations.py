@@ -153,3 +153,49 @@ def test_alibi_slope_of_kv_head_is_caught(monkeypatch):
         return None if s is None else s[(np.arange(len(s)) // w.group_size) * w.group_size]
     monkeypatch.setattr(po, "_slopes", wrong)
     _fails(pins.test_alibi_decode_closed_form)
+
+
+def _pins_blocks():
+    from tests import test_oracle_blocks as tb
+    return tb
+
+
+def test_unhashed_blocks_queued_at_tail_is_caught(monkeypatch, golden):
+    from oracle import block_pool as bpm
+
+    def wrong(self, blocks):
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0 and b != 0:
+                self.queue.append(b)              # partial blocks kept like cached ones
+    monkeypatch.setattr(bpm.BlockPoolModel, "free_blocks", wrong)
+    _fails(_pins_blocks().test_lru_model_hit_tokens, golden)
+
+
+def test_no_last_token_rule_is_caught(monkeypatch):
+    from oracle import block_pool as bpm
+    real = bpm.BlockPoolModel.allocate_prompt
+
+    def wrong(self, hashes, num_tokens, block_size):
+        return real(self, hashes, num_tokens + 1, block_size) if num_tokens % block_size == 0 \
+            else real(self, hashes, num_tokens, block_size)
+    monkeypatch.setattr(bpm.BlockPoolModel, "allocate_prompt", wrong)
+    _fails(_pins_blocks().test_last_token_is_always_computed)
+
+
+def test_touch_leaving_block_queued_is_caught(monkeypatch):
+    from oracle import block_pool as bpm
+
+    def wrong(self, blocks):
+        for b in blocks:
+            self.ref[b] += 1                      # forgot to take it off the queue
+    monkeypatch.setattr(bpm.BlockPoolModel, "touch", wrong)
+    _fails(_pins_blocks().test_pool_conservation_under_random_use)
+
+
+def test_hash_without_parent_is_caught(monkeypatch):
+    from oracle import block_pool as bpm
+    real = bpm.block_hash
+    monkeypatch.setattr(bpm, "block_hash", lambda parent, tokens, extra=0:
+                        real(bpm.NONE_HASH, tokens, extra))
+    _fails(_pins_blocks().test_block_hash_chain_property)
