@@ -215,6 +215,44 @@ int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits
                         int32_t max_num_partitions, void* stream);
 
 /*
+ * Choice between the single pass and split-KV for a decode batch (the role
+ * of P1 §3.3's V1/V2 condition, whose thresholds were set for NVIDIA SM
+ * counts; these were measured on MI355X with equal context lengths,
+ * Hq/Hkv 32/8 and 28/4, head_dim 128).  With U = num_reqs * num_kv_heads *
+ * ceil(G / 8) work units, L = max_seq_len and w = min(G, 8):
+ *     split  iff  U <= 64 and L * w >= 7168,
+ *            or   64 < U < 256 and L * w >= 14336;   otherwise single pass.
+ *     partition_size = 256 if U * L <= 2^16, 512 if U * L <= 2^17, else 1024.
+ * workspace_bytes is what pa_decode_auto needs for the plan (0 for the
+ * single pass).  Host-only.
+ */
+typedef struct pa_decode_plan {
+  int32_t split;              /* 0: pa_decode; 1: pa_decode_partitioned + merge */
+  int32_t partition_size;
+  int32_t max_num_partitions;
+  int32_t reserved;
+  size_t workspace_bytes;
+} pa_decode_plan;
+
+int pa_decode_plan_for(const pa_kv_layout* layout, int32_t num_reqs, int32_t num_q_heads,
+                       int32_t max_seq_len, pa_decode_plan* plan);
+
+/*
+ * Decode by a plan (pa_decode_plan_for's, or the caller's own): the single
+ * pass, or split-KV + merge with tmp_out, max_logits and exp_sums carved
+ * from `workspace` (caller-owned device memory, 256-byte aligned, at least
+ * plan->workspace_bytes; calls that overlap on one workspace race).
+ * Arguments otherwise as pa_decode; the result is the same.
+ */
+int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                   int32_t max_seq_len, float scale, const float* k_scale,
+                   const float* v_scale, const float* alibi_slopes,
+                   const pa_decode_plan* plan, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * Varlen (chunked) prefill over the paged cache (P2 §11.6: query_start_loc
  * as cu_seqlens_q, seq_lens as seqused_k, block_table for the paged K/V).
  * Request r owns query rows query_start_loc[r] .. query_start_loc[r+1]-1;

@@ -116,6 +116,20 @@ int pa_pool_commit(pa_block_pool* pool, const int32_t* block_ids, const uint64_t
  * first, P4 §10). */
 int pa_pool_free_request(pa_block_pool* pool, const int32_t* block_ids, int32_t n);
 
+/*
+ * Block-table entries for kernels whose block is smaller than the manager's
+ * ("vllm 深度解析：一切从 PagedAttention 谈起", BlockTable.map_to_kernel_blocks):
+ * a manager block of k kernel blocks (k = manager block size / 16) with id b
+ * covers kernel blocks b*k .. b*k + k - 1, so
+ *     out[i*k + j] = ids[i]*k + j,   i < n, j < k      (n*k entries).
+ * With the pool layout [kernel block][KV head][16][head_dim] a manager block
+ * is k consecutive kernel blocks.  Negative ids (padding) stay negative.
+ * Returns PA_OK, or PA_ERR_INVALID_ARG for k < 1, a NULL array or an id whose
+ * expansion overflows int32.
+ */
+int pa_map_to_kernel_blocks(const int32_t* ids, int32_t n, int32_t blocks_per_kv_block,
+                            int32_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,17 @@ def block_hashes(tokens, block_size: int, extra_key: int = 0) -> list:
     return out
 
 
+def map_to_kernel_blocks(ids, blocks_per_kv_block: int) -> list:
+    """Manager block b of k kernel blocks covers kernel blocks b*k .. b*k+k-1
+    (P3 BlockTable.map_to_kernel_blocks); padding (negative) stays as is."""
+    k = blocks_per_kv_block
+    out = []
+    for b in ids:
+        for j in range(k):
+            out.append(b if b < 0 else b * k + j)
+    return out
+
+
 class BlockPoolModel:
     """Plain-list model of the block pool (P3 BlockPool)."""
 

@@ -21,7 +21,7 @@ __all__ = [
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
-    "EXPORTED_SYMBOLS",
+    "PaDecodePlan", "pa_decode_plan_for", "pa_decode_auto", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,11 +42,12 @@ EXPORTED_SYMBOLS = (
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
+    "pa_decode_plan_for", "pa_decode_auto",
     # host block manager (include/pa_blocks.h; binding in blocks.py)
     "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
     "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
     "pa_pool_free_blocks", "pa_pool_cache_block", "pa_pool_allocate_prompt", "pa_pool_commit",
-    "pa_pool_free_request",
+    "pa_pool_free_request", "pa_map_to_kernel_blocks",
 )
 
 
@@ -54,6 +55,12 @@ class PaKvLayout(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("cache_dtype", ctypes.c_int32)]
+
+
+class PaDecodePlan(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("partition_size", ctypes.c_int32),
+                ("max_num_partitions", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class PaError(RuntimeError):
@@ -97,6 +104,9 @@ def lib() -> ctypes.CDLL:
             "pa_debug_gather_kv": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P], _I),
             "pa_debug_fp8_to_f32": ([_P, _P, _I, _P], _I),
             "pa_debug_fp8_to_f16": ([_P, _P, _I, _P], _I),
+            "pa_decode_plan_for": ([lp, _I, _I, _I, ctypes.POINTER(PaDecodePlan)], _I),
+            "pa_decode_auto": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
+                                ctypes.POINTER(PaDecodePlan), _P, ctypes.c_size_t, _P], _I),
             "pa_validate_metadata": ([_P, _I, _P, _P, _I, _P, _I, _I, _I], _I),
         }
         for name, (args, res) in sig.items():
@@ -180,6 +190,25 @@ def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_l
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
         _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
         _dev(alibi_slopes, "alibi_slopes"), _stream()), "pa_decode")
+
+
+def pa_decode_plan_for(layout, num_reqs: int, num_q_heads: int, max_seq_len: int) -> PaDecodePlan:
+    plan = PaDecodePlan()
+    _check(lib().pa_decode_plan_for(ctypes.byref(layout), int(num_reqs), int(num_q_heads),
+                                    int(max_seq_len), ctypes.byref(plan)), "pa_decode_plan_for")
+    return plan
+
+
+def pa_decode_auto(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
+                   scale: float, plan: PaDecodePlan, workspace=None, k_scale=None,
+                   v_scale=None, alibi_slopes=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_auto(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"),
+        ctypes.byref(plan), _dev(workspace, "workspace"), nbytes, _stream()), "pa_decode_auto")
 
 
 def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:

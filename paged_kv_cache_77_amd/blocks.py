@@ -32,6 +32,7 @@ _SIGS = {
     "pa_pool_allocate_prompt": ([_P, _P, _I, _I, _I, _P, _I, _P], _I),
     "pa_pool_commit": ([_P, _P, _P, _I], _I),
     "pa_pool_free_request": ([_P, _P, _I], _I),
+    "pa_map_to_kernel_blocks": ([_P, _I, _I, _P], _I),
 }
 _ready = False
 
@@ -73,6 +74,15 @@ def block_hashes(tokens: Sequence[int], block_size: int = 16, extra_key: int = 0
     if n < 0:
         raise PaError(n, "pa_block_hashes")
     return [int(x) for x in out[:n]]
+
+
+def map_to_kernel_blocks(ids: Sequence[int], blocks_per_kv_block: int) -> list:
+    """Kernel block ids of manager blocks of blocks_per_kv_block kernel blocks."""
+    a = _i32(ids)
+    out = np.zeros(max(1, len(a) * blocks_per_kv_block), dtype=np.int32)
+    _check(_lib().pa_map_to_kernel_blocks(_ptr(a), len(a), blocks_per_kv_block, _ptr(out)),
+           "pa_map_to_kernel_blocks")
+    return [int(x) for x in out[:len(a) * blocks_per_kv_block]]
 
 
 class BlockPool:

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -247,6 +248,69 @@ int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits
   return hip_status(pa::launch_merge(out, tmp_out, max_logits, exp_sums, seq_lens, num_reqs,
                                      num_q_heads, head_dim, partition_size,
                                      max_num_partitions, (hipStream_t)stream));
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static size_t split_workspace_bytes(int32_t num_reqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_num_partitions) {
+  const size_t rows = (size_t)num_reqs * num_q_heads * max_num_partitions;
+  return align256(rows * head_dim * 4) + 2 * align256(rows * 4);
+}
+
+int pa_decode_plan_for(const pa_kv_layout* layout, int32_t num_reqs, int32_t num_q_heads,
+                       int32_t max_seq_len, pa_decode_plan* plan) {
+  PA_TRY(check_layout(layout));
+  PA_TRY(check_heads(layout, num_q_heads));
+  if (num_reqs < 0 || max_seq_len < 0 || !plan) return PA_ERR_INVALID_ARG;
+  const int64_t G = num_q_heads / layout->num_kv_heads;
+  const int64_t units = (int64_t)num_reqs * layout->num_kv_heads * ((G + 7) / 8);
+  const int64_t L = max_seq_len, w = G < 8 ? G : 8;
+  memset(plan, 0, sizeof(*plan));
+  plan->split = ((units <= 64 && L * w >= 7168) || (units > 64 && units < 256 && L * w >= 14336))
+                    ? 1 : 0;
+  const int64_t work = units * L;
+  plan->partition_size = work <= (1 << 16) ? 256 : work <= (1 << 17) ? 512 : 1024;
+  plan->max_num_partitions = (int32_t)std::max<int64_t>(
+      1, (L + plan->partition_size - 1) / plan->partition_size);
+  plan->workspace_bytes = plan->split ? split_workspace_bytes(num_reqs, num_q_heads,
+                                                              layout->head_dim,
+                                                              plan->max_num_partitions)
+                                      : 0;
+  return PA_OK;
+}
+
+int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                   int32_t max_seq_len, float scale, const float* k_scale, const float* v_scale,
+                   const float* alibi_slopes, const pa_decode_plan* plan, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!plan) return PA_ERR_INVALID_ARG;
+  if (!plan->split)
+    return pa_decode(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                     bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale, alibi_slopes,
+                     stream);
+  PA_TRY(check_layout(layout));
+  if (num_reqs == 0) return PA_OK;
+  const size_t need = split_workspace_bytes(num_reqs, num_q_heads, layout->head_dim,
+                                            plan->max_num_partitions);
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need ||
+      !out || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  const size_t rows = (size_t)num_reqs * num_q_heads * plan->max_num_partitions;
+  char* base = reinterpret_cast<char*>(workspace);
+  float* tmp = reinterpret_cast<float*>(base);
+  float* ml = reinterpret_cast<float*>(base + align256(rows * layout->head_dim * 4));
+  float* es = reinterpret_cast<float*>(base + align256(rows * layout->head_dim * 4) +
+                                       align256(rows * 4));
+  PA_TRY(pa_decode_partitioned(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                               bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                               alibi_slopes, plan->partition_size, plan->max_num_partitions, tmp,
+                               ml, es, stream));
+  return pa_merge_partitions(out, tmp, ml, es, seq_lens, num_reqs, num_q_heads,
+                             layout->head_dim, plan->partition_size, plan->max_num_partitions,
+                             stream);
 }
 
 int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int32_t num_tokens,

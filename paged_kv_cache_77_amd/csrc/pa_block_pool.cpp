@@ -252,4 +252,16 @@ int pa_pool_free_request(pa_block_pool* pool, const int32_t* block_ids, int32_t 
   return pa_pool_free_blocks(pool, rev.data(), n);
 }
 
+int pa_map_to_kernel_blocks(const int32_t* ids, int32_t n, int32_t blocks_per_kv_block,
+                            int32_t* out) {
+  const int32_t k = blocks_per_kv_block;
+  if (n < 0 || k < 1 || (n > 0 && (!ids || !out))) return PA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] >= 0 && (int64_t)ids[i] * k + (k - 1) > INT32_MAX) return PA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < k; ++j)
+      out[(int64_t)i * k + j] = ids[i] < 0 ? ids[i] : ids[i] * k + j;
+  return PA_OK;
+}
+
 }  // extern "C"

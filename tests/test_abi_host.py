@@ -155,3 +155,38 @@ def test_balanced_workspace_size_and_checks():
     big = pa.pa_decode_workspace_size(lay, 5000, 32)
     assert L.pa_decode_balanced(ctypes.byref(lay), p, p, 5000, 32, p, p, p, 256, p, 4096, 0.1,
                                 None, None, None, p, big, None) == pa.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("R,hq,hkv,L,split,P", [
+    (1, 32, 8, 8192, 1, 256),      # 8 units, long context: split
+    (8, 32, 8, 1024, 0, 256),      # 64 units, L*w = 4096 < 7168: single
+    (8, 32, 8, 2048, 1, 512),      # 64 units, L*w = 8192: split
+    (16, 32, 8, 4096, 1, 1024),    # 128 units, L*w = 16384 >= 14336
+    (16, 32, 8, 2048, 0, 1024),    # 128 units, L*w = 8192 < 14336
+    (32, 28, 4, 2048, 1, 1024),    # G = 7: 128 units, L*w = 14336
+    (32, 32, 8, 32768, 0, 1024),   # 256 units: always single
+    (64, 32, 8, 4096, 0, 1024),
+    (1, 64, 4, 4096, 1, 256),      # G = 16: two head chunks per KV head (8 units)
+])
+def test_decode_plan_rule(R, hq, hkv, L, split, P):
+    lay = pa.make_layout(100, hkv, 128, 0)
+    plan = pa.pa_decode_plan_for(lay, R, hq, L)
+    assert (plan.split, plan.partition_size) == (split, P)
+    assert plan.max_num_partitions == max(1, -(-L // P))
+    if split:
+        rows = R * hq * plan.max_num_partitions
+        assert plan.workspace_bytes >= rows * 128 * 4 + 2 * rows * 4
+    else:
+        assert plan.workspace_bytes == 0
+
+
+def test_decode_auto_rejects_small_workspace():
+    L = pa.lib()
+    lay = pa.make_layout(100, 8, 128, 0)
+    plan = pa.pa_decode_plan_for(lay, 1, 32, 8192)
+    p = ctypes.c_void_p(4096)
+    assert L.pa_decode_auto(ctypes.byref(lay), p, p, 1, 32, p, p, p, 512, p, 8192, 0.1, None,
+                            None, None, ctypes.byref(plan), p, plan.workspace_bytes - 1,
+                            None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_decode_auto(ctypes.byref(lay), p, p, 1, 32, p, p, p, 512, p, 8192, 0.1, None,
+                            None, None, None, p, 0, None) == pa.PA_ERR_INVALID_ARG

@@ -89,3 +89,17 @@ def test_errors_leave_the_pool_unchanged():
     c.free_blocks(got)
     assert c.num_free() == 4 and c.ref_count(0) == 0 and c.usage() == 0.0
     assert c.ref_count(99) == -1
+
+
+def test_map_to_kernel_blocks_matches_oracle(golden):
+    (k, ids, want), = golden("kernel_blocks.txt")
+    assert pb.map_to_kernel_blocks([int(x) for x in ids.split()], int(k)) == \
+        [int(x) for x in want.split()]
+    rng = np.random.default_rng(5)
+    for k in (1, 2, 3, 8):
+        ids = rng.integers(-2, 1000, size=33).tolist()
+        assert pb.map_to_kernel_blocks(ids, k) == bp.map_to_kernel_blocks(ids, k)
+    with pytest.raises(pa.PaError):
+        pb.map_to_kernel_blocks([1], 0)
+    with pytest.raises(pa.PaError):
+        pb.map_to_kernel_blocks([1 << 30], 4)

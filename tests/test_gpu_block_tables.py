@@ -96,3 +96,44 @@ def test_prefix_sharing_tables_from_the_block_manager():
         pool.free_request(row)
     pool.free_request(row0)
     assert pool.num_free() == NB - 1 and pool.lookup(h0[3]) == row0[3]
+
+
+def test_manager_blocks_of_two_kernel_blocks_decode():
+    """A manager with 32-token blocks: its rows expand to 16-token kernel
+    blocks (map_to_kernel_blocks); every context is written through the
+    expanded table (fused write) and decoded; GPU vs oracle."""
+    print("\n[case] 32-token manager blocks -> kernel blocks -> write + decode", flush=True)
+    k, NBM = 2, 40
+    pool = pb.BlockPool(NBM, caching=False)
+    ctx = [1, 31, 32, 33, 200, 64]
+    rows = [pb.map_to_kernel_blocks(pool.allocate_prompt([], n, 32)[0], k) for n in ctx]
+    assert all(len(r) == 2 * -(-n // 32) for r, n in zip(rows, ctx))
+    R, T = len(ctx), sum(ctx)
+    W = max(len(r) for r in rows)
+    bt = np.full((R, W), wl.TABLE_PAD, np.int32)
+    for r, row in enumerate(rows):
+        bt[r, :len(row)] = row
+    rng = np.random.default_rng(12)
+    seq = np.array(ctx, np.int32)
+    qsl = np.zeros(R + 1, np.int32)
+    qsl[1:] = np.cumsum(seq)
+    nb = NBM * k
+    w = wl.Workload(name="kblocks", num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_size=B,
+                    cache_dtype="bf16", seq_lens=seq, q_lens=seq.copy(), query_start_loc=qsl,
+                    block_table=bt, num_blocks=nb,
+                    k_pool=np.full((nb, HKV, B, D), wl.BF16_NAN, np.uint16),
+                    v_pool=np.full((nb, HKV, B, D), wl.BF16_NAN, np.uint16),
+                    q=wl.to_bf16_bits(rng.standard_normal((R, HQ, D), dtype=np.float32)),
+                    k_new=wl.to_bf16_bits(rng.standard_normal((T, HKV, D), dtype=np.float32)),
+                    v_new=wl.to_bf16_bits(rng.standard_normal((T, HKV, D), dtype=np.float32)),
+                    scale=np.float32(1 / np.sqrt(D)), k_scale=np.float32(1),
+                    v_scale=np.float32(1), writes_new_kv=True, seed=12)
+    d = dv.to_device(w)
+    dv.write_new_kv_fused(d, None)
+    out = torch.full((R, HQ, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dv.run_decode(d, out)
+    torch.cuda.synchronize()
+    sm = oracle.slot_mapping(bt, qsl, seq, B)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, sm, B)
+    assert np.array_equal(dv.bits_of(d.k_cache), kp)
+    check_bf16(dv.bits_of(out), oracle.decode(w, k_pool=kp, v_pool=vp), "kernel-block decode")

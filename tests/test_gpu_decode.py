@@ -273,3 +273,23 @@ def test_fp8_decode_after_quantising_write():
     dv.run_decode(d, out)
     torch.cuda.synchronize()
     check_bf16(dv.bits_of(out), oracle.decode(w, k_pool=kp, v_pool=vp), "fp8 write + decode")
+
+
+@pytest.mark.parametrize("ctx,hq,hkv", [([9000, 17, 4097], 32, 8), ([300, 1, 2500] * 30, 32, 8),
+                                        ([5000, 64], 28, 4)])
+def test_decode_auto_follows_its_plan(ctx, hq, hkv):
+    """pa_decode_auto with pa_decode_plan_for's plan (split-KV for the few
+    long requests, single pass for the wide batch) against the oracle."""
+    _announce(f"decode auto ctx={ctx[:3]}... hq={hq} hkv={hkv}")
+    w = wl.make_workload(name="t", seq_lens=ctx, q_lens=[1] * len(ctx), num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=128, seed=80 + len(ctx),
+                         writes_new_kv=False)
+    d = dv.to_device(w)
+    plan = pa.pa_decode_plan_for(d.layout, w.num_reqs, hq, d.max_seq_len)
+    assert plan.split == (1 if len(ctx) <= 3 else 0)
+    ws = torch.empty((max(plan.workspace_bytes, 1),), dtype=torch.uint8, device="cuda")
+    out = _out(w)
+    pa.pa_decode_auto(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                      d.max_seq_len, float(w.scale), plan, ws)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(out), oracle.decode(w), "decode auto")

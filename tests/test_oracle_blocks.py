@@ -134,3 +134,24 @@ def test_pool_conservation_under_random_use():
         assert m.num_free() + sum(1 for b in range(1, 64) if m.ref[b] > 0) == 63
         assert all(m.ref[b] == 0 for b in m.queue) and len(set(m.queue)) == len(m.queue)
         assert held == sum(len(r) for r in live)
+
+
+def test_map_to_kernel_blocks_page_example(golden):
+    (k, ids, want), = golden("kernel_blocks.txt")
+    ids = [int(x) for x in ids.split()]
+    assert bp.map_to_kernel_blocks(ids, int(k)) == [int(x) for x in want.split()]
+
+
+def test_map_to_kernel_blocks_covers_the_same_tokens():
+    """Token t of a request sits in manager block t // (16k), kernel block
+    t // 16: the expanded row must name the kernel block that holds it."""
+    rng = np.random.default_rng(4)
+    for k in (1, 2, 4):
+        ids = rng.permutation(50)[:7].tolist()
+        row = bp.map_to_kernel_blocks(ids, k)
+        assert len(row) == 7 * k
+        for t in range(7 * 16 * k):
+            mgr = ids[t // (16 * k)]
+            within = (t % (16 * k)) // 16           # kernel block inside the manager block
+            assert row[t // 16] == mgr * k + within
+    assert bp.map_to_kernel_blocks([3, -1], 2) == [6, 7, -1, -1]
