@@ -203,6 +203,25 @@ int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num
                           void* stream);
 
 /*
+ * Split-KV decode over a range of partitions: as pa_decode_partitioned but
+ * only partitions p with part_begin <= p < part_end (and p < ceil(seq_len/P))
+ * are written; 0 <= part_begin <= part_end <= max_num_partitions.  Calls on
+ * disjoint ranges fill one set of partial arrays, merged once by
+ * pa_merge_partitions -- the building block of sharding a long context by
+ * token range (each device computes its partitions; the partials are
+ * gathered; the merge of P1 §3.2.9 is associative).
+ */
+int pa_decode_partitioned_range(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
+                                int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t bt_stride,
+                                const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                const float* k_scale, const float* v_scale,
+                                const float* alibi_slopes, int32_t partition_size,
+                                int32_t max_num_partitions, int32_t part_begin,
+                                int32_t part_end, float* tmp_out, float* max_logits,
+                                float* exp_sums, void* stream);
+
+/*
  * Split-KV decode, merge stage (P1 §3.2.9 equations):
  *     m = max_j m_j,  L = sum_j l_j e^(m_j - m),
  *     out = sum_j tmp_out_j * l_j e^(m_j - m) / L     -> bf16, round to nearest even

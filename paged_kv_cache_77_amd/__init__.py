@@ -21,7 +21,8 @@ __all__ = [
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
-    "PaDecodePlan", "pa_decode_plan_for", "pa_decode_auto", "EXPORTED_SYMBOLS",
+    "PaDecodePlan", "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
+    "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "pa_decode_workspace_size", "pa_decode_balanced",
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
-    "pa_decode_plan_for", "pa_decode_auto",
+    "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
     # host block manager (include/pa_blocks.h; binding in blocks.py)
     "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
     "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
             "pa_decode_partitioned": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
                                        _I, _I, _P, _P, _P, _P], _I),
             "pa_merge_partitions": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+            "pa_decode_partitioned_range": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
+                                             _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
             "pa_prefill_varlen": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                    _F, _P, _P, _P, _P], _I),
             "pa_debug_gather_kv": ([lp, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P], _I),
@@ -240,6 +243,20 @@ def pa_decode_partitioned(layout, q, k_cache, v_cache, block_table, seq_lens,
         max_logits.shape[2],
         _dev(tmp_out, "tmp_out"), _dev(max_logits, "max_logits"), _dev(exp_sums, "exp_sums"),
         _stream()), "pa_decode_partitioned")
+
+
+def pa_decode_partitioned_range(layout, q, k_cache, v_cache, block_table, seq_lens,
+                                max_seq_len: int, scale: float, partition_size: int,
+                                part_begin: int, part_end: int, tmp_out, max_logits, exp_sums,
+                                k_scale=None, v_scale=None, alibi_slopes=None) -> None:
+    _check(lib().pa_decode_partitioned_range(
+        ctypes.byref(layout), _dev(q, "q"), q.shape[0], q.shape[1], _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_table, "block_table"), block_table.shape[1],
+        _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale), _dev(k_scale, "k_scale"),
+        _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"), int(partition_size),
+        max_logits.shape[2], int(part_begin), int(part_end), _dev(tmp_out, "tmp_out"),
+        _dev(max_logits, "max_logits"), _dev(exp_sums, "exp_sums"), _stream()),
+        "pa_decode_partitioned_range")
 
 
 def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,

@@ -55,10 +55,14 @@ def _check(status: int, where: str) -> None:
 
 
 def _i32(a) -> np.ndarray:
+    if isinstance(a, np.ndarray) and a.dtype == np.int32:
+        return np.ascontiguousarray(a)
     return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
 
 
 def _u64(a) -> np.ndarray:
+    if isinstance(a, np.ndarray) and a.dtype == np.uint64:
+        return np.ascontiguousarray(a)
     return np.ascontiguousarray(np.asarray([int(x) for x in a], dtype=np.uint64))
 
 
@@ -144,7 +148,7 @@ class BlockPool:
                                               block_size, _ptr(out), nblk,
                                               ctypes.byref(cached)),
                "pa_pool_allocate_prompt")
-        return [int(x) for x in out[:nblk]], int(cached.value)
+        return out[:nblk].tolist(), int(cached.value)
 
     def commit(self, blocks, hashes) -> None:
         b, hs = _i32(blocks), _u64(hashes)

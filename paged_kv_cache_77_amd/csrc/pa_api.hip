@@ -236,6 +236,38 @@ int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num
   return hip_status(pa::launch_decode(a, true, (hipStream_t)stream));
 }
 
+int pa_decode_partitioned_range(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
+                                int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t bt_stride,
+                                const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                const float* k_scale, const float* v_scale,
+                                const float* alibi_slopes, int32_t partition_size,
+                                int32_t max_num_partitions, int32_t part_begin,
+                                int32_t part_end, float* tmp_out, float* max_logits,
+                                float* exp_sums, void* stream) {
+  PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                       bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
+  if (partition_size <= 0 || partition_size % layout->block_size != 0)
+    return PA_ERR_INVALID_ARG;
+  const int64_t need = ((int64_t)max_seq_len + partition_size - 1) / partition_size;
+  if (max_num_partitions < 1 || max_num_partitions < need) return PA_ERR_INVALID_ARG;
+  if (part_begin < 0 || part_end < part_begin || part_end > max_num_partitions)
+    return PA_ERR_INVALID_ARG;
+  if (num_reqs == 0 || part_end == part_begin) return PA_OK;
+  if (!tmp_out || !max_logits || !exp_sums || !aligned16(tmp_out)) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
+                                 block_table, bt_stride, seq_lens, max_seq_len, scale,
+                                 k_scale, v_scale, alibi_slopes);
+  a.tmp_out = tmp_out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.partition_size = partition_size;
+  a.max_num_partitions = max_num_partitions;
+  a.part_begin = part_begin;
+  a.part_end = part_end;
+  return hip_status(pa::launch_decode(a, true, (hipStream_t)stream));
+}
+
 int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

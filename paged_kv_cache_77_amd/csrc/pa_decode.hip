@@ -513,8 +513,9 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART>())) vo
   }
   const int seq_len = a.seq_lens[r];
   int t_begin = 0, t_end = seq_len;
+  const int part = a.part_begin + (int)blockIdx.x;     // partition index (PART)
   if constexpr (PART) {
-    t_begin = blockIdx.x * a.partition_size;
+    t_begin = part * a.partition_size;
     if (t_begin >= seq_len) return;
     t_end = min(seq_len, t_begin + a.partition_size);
   }
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART>())) vo
     O = O / L * vs;
     const int h = h0 + j;
     if constexpr (PART) {
-      const int64_t idx = ((int64_t)r * a.num_q_heads + h) * a.max_num_partitions + blockIdx.x;
+      const int64_t idx = ((int64_t)r * a.num_q_heads + h) * a.max_num_partitions + part;
       a.tmp_out[idx * D + dd] = O;
       if (dd == 0) {       // re-based on the exact max: (m, l) as the pages define them
         a.max_logits[idx] = Mt * kLn2;
@@ -936,8 +937,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
   constexpr int PD = PA_DECODE_PREFETCH;
   if (partitioned) {
     constexpr int WAVES = PA_DECODE_WAVES_SPLIT;
-    const int nparts = (a.max_seq_len + a.partition_size - 1) / a.partition_size;
-    if (nparts == 0) return hipSuccess;
+    int nparts = (a.max_seq_len + a.partition_size - 1) / a.partition_size;
+    if (a.part_end > 0) nparts = min(nparts, a.part_end) - a.part_begin;
+    if (nparts <= 0) return hipSuccess;
     dim3 grid(nparts, a.num_kv_heads * n_chunks, a.num_reqs);
     hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, true, PD>), grid, dim3(WAVES * 64), 0, st,
                        a, n_chunks);

@@ -26,6 +26,7 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t partition_size;           // tokens per partition (partitioned mode)
   int32_t max_num_partitions;
+  int32_t part_begin, part_end;     // partitioned mode: partitions written (end 0 = all)
   int32_t lpt;                      // set by the launcher: longest requests first
   float scale;
 };

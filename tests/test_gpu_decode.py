@@ -293,3 +293,29 @@ def test_decode_auto_follows_its_plan(ctx, hq, hkv):
                       d.max_seq_len, float(w.scale), plan, ws)
     torch.cuda.synchronize()
     check_bf16(dv.bits_of(out), oracle.decode(w), "decode auto")
+
+
+def test_partition_ranges_merge_like_one_call():
+    """Context-parallel building block: split-KV over disjoint partition
+    ranges (as separate devices would compute them) fills the same partial
+    arrays; one merge then equals the single split-KV call bit for bit."""
+    _announce("partition ranges + one merge")
+    w = wl.config_workload(3, scale_down=4)            # 2 requests x 8192 tokens
+    d = dv.to_device(w)
+    P = 512
+    full = _out(w)
+    tmp, ml, es = dv.run_decode_partitioned(d, full, P)
+    pmax = ml.shape[2]
+    tmp2 = torch.full_like(tmp, float("nan"))
+    ml2 = torch.full_like(ml, float("nan"))
+    es2 = torch.full_like(es, float("nan"))
+    for lo, hi in ((0, 5), (5, 6), (6, pmax)):          # uneven ranges, one of one partition
+        pa.pa_decode_partitioned_range(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
+                                       d.seq_lens, d.max_seq_len, float(w.scale), P, lo, hi,
+                                       tmp2, ml2, es2)
+    out = _out(w)
+    pa.pa_merge_partitions(out, tmp2, ml2, es2, d.seq_lens, P)
+    torch.cuda.synchronize()
+    assert torch.equal(tmp2, tmp) and torch.equal(ml2, ml) and torch.equal(es2, es)
+    assert np.array_equal(dv.bits_of(out), dv.bits_of(full))
+    check_bf16(dv.bits_of(out), oracle.decode(w), "range merge")
