@@ -55,20 +55,22 @@ constexpr float kTau = 8.0f;
 #ifndef PA_DECODE_PREFETCH
 #define PA_DECODE_PREFETCH 1
 #endif
-// Minimum waves per SIMD the single-pass decode kernel is compiled for (caps
-// its VGPRs): bf16 kernels with up to 4 heads per chunk fit 3 waves per SIMD
-// (168 VGPRs) without spilling (measured 1% faster on the batched workload);
-// the split-KV variant spills at that cap and is left to the compiler.
+// Minimum waves per SIMD the 8-wave single-pass decode kernel is compiled for
+// (caps its VGPRs): bf16 kernels with up to 4 heads per chunk fit 3 waves per
+// SIMD (168 VGPRs) without spilling (measured 1% faster on the batched
+// workload); the 4-wave and split-KV variants measured slower with the cap.
 #ifndef PA_DECODE_MIN_WAVES_EU
 #define PA_DECODE_MIN_WAVES_EU 3
 #endif
-// Longest-first order of the single pass's work-groups (0 disables).
+// Longest-first order of the single pass's work-groups (0 disables), used for
+// batches of up to kLptMaxReqs requests.
 #ifndef PA_DECODE_LPT
 #define PA_DECODE_LPT 1
 #endif
-template <int GC, bool FP8, bool PART>
+constexpr int kLptMaxReqs = 128;
+template <int GC, bool FP8, bool PART, int WAVES>
 constexpr int decode_min_waves() {
-  return (!FP8 && !PART && GC <= 4) ? PA_DECODE_MIN_WAVES_EU : 1;
+  return (!FP8 && !PART && GC <= 4 && WAVES == 8) ? PA_DECODE_MIN_WAVES_EU : 1;
 }
 
 template <int D, int GC, bool FP8>
@@ -470,7 +472,7 @@ struct DecodeSmem {
 // PART: false -> write the final bf16 output; true -> write the partition
 // partials.  Rows of varlen batches come from query_start_loc when given.
 template <int D, int GC, bool FP8, int WAVES, bool PART, int PD>
-__global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART>())) void decode_kernel(
+__global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>())) void decode_kernel(
     DecodeArgs a, int n_chunks) {
   using Dec = WaveDecoder<D, GC, FP8>;
   __shared__ DecodeSmem<D, GC, FP8, WAVES> sm;
@@ -948,7 +950,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     dim3 grid(1, a.num_kv_heads * n_chunks, a.num_reqs);
     const int64_t groups = (int64_t)grid.y * grid.z;
     DecodeArgs b = a;
-    b.lpt = (PA_DECODE_LPT && a.query_start_loc == nullptr && a.num_reqs <= kBtChunk) ? 1 : 0;
+    // (the rank search costs O(num_reqs) per thread: kept to modest batches)
+    b.lpt = (PA_DECODE_LPT && a.query_start_loc == nullptr && a.num_reqs <= kLptMaxReqs) ? 1 : 0;
     if (groups < 768) {
       constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
       hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,

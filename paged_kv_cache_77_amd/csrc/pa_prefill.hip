@@ -6,8 +6,9 @@
 // seq_len - q_len + i and attends keys 0..position (causal), K/V read through
 // block_table[r][t / 16].  With ALiBi slopes the score of key t for the query
 // at position p gains slope_h * (t - p): the decode term of "vLLM 深度解析
-// （二）" §3.2.4, slope_h * (t - seq_len + 1), is this for p = seq_len - 1.  Tiles of keys are folded in with the running
-// (m, l, A) state, so S and P never reach HBM (§2.1/§2.2 of the second page).
+// （二）" §3.2.4, slope_h * (t - seq_len + 1), is this for p = seq_len - 1.
+// Tiles of keys are folded in with the running (m, l, A) state, so S and P
+// never reach HBM (§2.1/§2.2 of the second page).
 // Rows of requests with q_len <= 1 are left to the decode kernel.
 //
 // Work-group: (request, KV head, query tile, head chunk).  Its 4 waves share
@@ -87,7 +88,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   const int seq_len = a.seq_lens[r];
   const int pos0 = seq_len - q_len;                         // position of query 0
 
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  // the wave index is uniform: keep it (and all per-wave values) scalar
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lq = lane % 32, lh = lane / 32;
   const int hw = w % hpw, qbl = w / hpw;                    // head and query block of the wave
   const bool wave_on = (qbl < qbw) && (hc * kWaves + hw < G);
@@ -244,13 +246,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
       }
       // -- causal mask by select (diagonal tiles only), tile max
       if (k0 + kBN - 1 > wave_pmin) {
+        // key k0 + c (c = 32b + 8(v/4) + 4lh + v%4) is visible iff c <= p_q - k0
+        const int lim = p_q - k0 - 4 * lh;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int t = k0 + 32 * b + 8 * (v / 4) + 4 * lh + (v % 4);
-            s[b][v] = (t <= p_q) ? s[b][v] : -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v)
+            s[b][v] = (32 * b + 8 * (v / 4) + (v % 4) <= lim) ? s[b][v] : -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
