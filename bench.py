@@ -111,7 +111,8 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
                       f"{w.num_reqs} requests, all heads) in {dt:.1f} s, fp64 numpy"}
 
 
-def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int) -> dict:
+def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
+            cold_reps: int = 30) -> dict:
     """Run `warmup` untimed then `steps` timed steps of workload `cfg`."""
     import numpy as np
     import torch
@@ -171,10 +172,33 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int) -
         step(True)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    warm = sorted(a.elapsed_time(b) for a, b in ev)
+    kern_ms = sum(warm) / len(warm)
+
+    # cold-cache timing of the same kernel(s): a 1 GiB write between
+    # launches evicts L2 and the 256 MB Infinity Cache (MALL)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold_ev = []
+    for _ in range(cold_reps):
+        flush.fill_(1.0)
+        n0 = len(ev)
+        step(True)
+        cold_ev.append(ev[n0])
+    torch.cuda.synchronize()
+    cold = sorted(a.elapsed_time(b) for a, b in cold_ev)
+    del flush
+
+    def pct(v, q):
+        return round(v[min(len(v) - 1, int(q * len(v)))], 5)
     r = {"cfg": cfg, "w": w, "nbytes": nbytes, "ms_step": ms_step, "kern_ms": kern_ms,
          "path": "varlen" if is_prefill else path,
-         "partition_size": P if (path == "split" and not is_prefill) else None}
+         "partition_size": P if (path == "split" and not is_prefill) else None,
+         "kernel_ms_stats": {
+             "warm": {"median": pct(warm, 0.5), "p10": pct(warm, 0.1), "p90": pct(warm, 0.9),
+                      "reps": len(warm)},
+             "cold": ({"median": pct(cold, 0.5), "p10": pct(cold, 0.1), "p90": pct(cold, 0.9),
+                       "reps": len(cold), "flush": "1 GiB device write before each launch"}
+                      if cold else None)}}
 
     if is_prefill:
         # the prefill row alone (q_len > 1), timed with events around its launch
@@ -241,6 +265,7 @@ def roofline_of(r) -> dict:
     return {"bound": "hbm", "kernel": r["kernel"], "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic_for(r["key"]), "kernel_ms": round(r["kern_ms"], 5),
+            "kernel_ms_stats": r["kernel_ms_stats"],
             "algorithmic_bytes_per_launch": r["kbytes"]}
 
 

@@ -68,6 +68,10 @@ constexpr float kTau = 8.0f;
 #define PA_DECODE_LPT 1
 #endif
 constexpr int kLptMaxReqs = 128;
+// FP8 decode on the matrix cores for G >= 4 (0: always the vector-ALU kernel).
+#ifndef PA_DECODE_FP8_MFMA
+#define PA_DECODE_FP8_MFMA 1
+#endif
 template <int GC, bool FP8, bool PART, int WAVES>
 constexpr int decode_min_waves() {
   return (!FP8 && !PART && GC <= 4 && WAVES == 8) ? PA_DECODE_MIN_WAVES_EU : 1;
@@ -1019,6 +1023,10 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int mode, void* ws, hipSt
 static hipError_t launch_any(const DecodeArgs& a, int mode, void* ws, hipStream_t st) {
   if (a.num_reqs == 0) return hipSuccess;
   const bool fp8 = a.cache_dtype != 0;
+  // FP8 caches with groups of 4+ query heads: the MFMA kernel (the vector-ALU
+  // kernel is the limit there, not memory)
+  if (PA_DECODE_FP8_MFMA && fp8 && mode != 2 && a.num_q_heads / a.num_kv_heads >= 4)
+    return launch_decode_mfma(a, mode == 1, st);
   if (a.head_dim == 64)
     return fp8 ? launch_decode_d<64, true>(a, mode, ws, st)
                : launch_decode_d<64, false>(a, mode, ws, st);

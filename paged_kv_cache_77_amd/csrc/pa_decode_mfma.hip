@@ -1,0 +1,347 @@
+// FP8-cache paged decode on the matrix cores (gfx950).
+//
+// Same result as decode_kernel ("vLLM 深度解析（二）：PagedAttention 核心机制"
+// §3.2: block-table walk, scaled q.k of the query heads sharing a KV head,
+// masked tail, softmax, PV; §2.2: the running (m, l, A) state; §3.2.7 for the
+// split-KV partials).  With an FP8 cache the shared-prefix workloads are not
+// memory-bound -- the vector ALU was the limit -- so the two products of a
+// 16-token block run as MFMAs with the GQA group's query heads on the N side
+// (16 per chunk; unused columns are zero queries):
+//
+//   S^T[16 tokens x 16 heads]  = K . Q^T   v_mfma_f32_16x16x32_bf16, D/32 steps;
+//       lane l supplies K row (token) l%16, d = (D/4)(l/16) + 8s .. +8 for step
+//       s, so its D/4 contiguous codes are one load; Q^T is permuted alike.
+//       The accumulator leaves lane l with tokens 4(l/16)+i of head l%16.
+//   O^T[D x 16 heads] += V^T . P^T          v_mfma_f32_16x16x16_f16, D/16 steps;
+//       P^T is the lane's own four probabilities (f16), V^T row m of d-block
+//       db is d = (D/16)m + db, so lane l loads D/16 contiguous codes of each
+//       of its four tokens and byte-shuffles them into f16 pairs (exact).
+//       The accumulator leaves lane l with d = (D/4)(l/16) + (D/16)i + db of
+//       head l%16 -- the same head as its softmax state.
+//
+// FP8 codes convert exactly to bf16 (K) and f16 (V); probabilities are f16
+// for the PV product (relative error <= 2^-11 per weight), l and the
+// max stay fp32.  Softmax in log2 units with the lazy running max of
+// decode_kernel.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMHeads = 16;       // query heads per chunk (the MFMA N side)
+constexpr int kMWaves = 4;
+constexpr int kMBtChunk = 1024;
+constexpr float kMTau = 8.0f;
+
+template <int D>
+struct MfmaDecodeSmem {
+  int32_t bt[kMBtChunk];
+  float m[kMWaves][kMHeads];
+  float mt[kMWaves][kMHeads];
+  float l[kMWaves][kMHeads];
+  float acc[kMWaves][kMHeads][D];
+};
+
+template <int D>
+struct MTile {
+  uint4 k[D / 64];               // D/4 codes of one K row (16 bytes each)
+  uint32_t v[4][D / 64];         // D/16 codes of each of four V rows
+};
+
+template <int D>
+__device__ __forceinline__ void mload(MTile<D>& t, const uint8_t* kbase, const uint8_t* vbase,
+                                      int32_t phys, int g, int num_kv_heads, int lane) {
+  const int64_t off = tile_offset(phys, g, num_kv_heads, D);      // bytes (1 per code)
+  const int row = lane % 16, grp = lane / 16;
+  const uint8_t* kp = kbase + off + row * D + (D / 4) * grp;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + 16 * c);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint8_t* vp = vbase + off + (4 * grp + e) * D + (D / 16) * row;
+    if constexpr (D / 64 == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(vp);
+      t.v[e][0] = w.x;
+      t.v[e][1] = w.y;
+    } else {
+      t.v[e][0] = *reinterpret_cast<const uint32_t*>(vp);
+    }
+  }
+}
+
+template <int D>
+struct MfmaDecoder {
+  static constexpr int KS = D / 32;       // QK steps
+  static constexpr int DB = D / 16;       // PV d-blocks
+  int lane, col, grp;
+  bool has_alibi;
+  float qk_scale, alibi;
+  int pos_q;
+  uint32_t qf[KS][4];                     // Q^T operand: 8 bf16 per step
+  float m_run, m_true, l_part;            // head col (replicated in the 4 lane groups)
+  f32x4_t oacc[DB];                       // MFMA accumulators, used in place
+
+  __device__ __forceinline__ void init(int lane_, float qk_scale_, bool has_alibi_) {
+    lane = lane_;
+    col = lane % 16;
+    grp = lane / 16;
+    qk_scale = qk_scale_;
+    has_alibi = has_alibi_;
+    alibi = 0.f;
+    pos_q = 0;
+  }
+
+  // q of row row_q, heads h0 .. h0+nh-1 (column col; others zero)
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row_q, int num_q_heads,
+                                         int h0, int nh, const float* slopes, int seq_len) {
+    const bool real = col < nh;
+    const uint16_t* qh = q + (row_q * num_q_heads + h0 + (real ? col : 0)) * D + (D / 4) * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * s);
+      qf[s][0] = real ? v.x : 0u;
+      qf[s][1] = real ? v.y : 0u;
+      qf[s][2] = real ? v.z : 0u;
+      qf[s][3] = real ? v.w : 0u;
+    }
+    pos_q = seq_len - 1;
+    if (has_alibi) alibi = real ? slopes[h0 + col] * kLog2e : 0.f;
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    m_true = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) oacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ __forceinline__ void compute(const MTile<D>& t, int tok0, int t_end) {
+    // -- S^T = K Q^T
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const uint4 raw = t.k[st / 2];
+      const uint32_t w0 = (st & 1) ? raw.z : raw.x;
+      const uint32_t w1 = (st & 1) ? raw.w : raw.y;
+      const f32x4_t a = fp8x4_to_f32(w0), b = fp8x4_to_f32(w1);
+      const uint4 kb = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                  pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+      const uint4 qb = make_uint4(qf[st][0], qf[st][1], qf[st][2], qf[st][3]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
+                                                  __builtin_bit_cast(bf16x8_t, qb), s, 0, 0, 0);
+    }
+    // -- scaled scores of tokens tok0 + 4grp + i, masked by select
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + 4 * grp + i;
+      float xv = s[i] * qk_scale;
+      if (has_alibi) xv = fmaf(alibi, (float)(tok - pos_q), xv);
+      x[i] = tok < t_end ? xv : -INFINITY;
+      bm = fmaxf(bm, x[i]);
+    }
+    bm = fmaxf(bm, xor_lanes(bm, 16));
+    bm = fmaxf(bm, xor_lanes(bm, 32));            // max over the head's 16 tokens
+    m_true = fmaxf(m_true, bm);
+    const bool grow = bm > m_run + kMTau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform and rare: move the max
+      const float m_new = grow ? bm : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) oacc[b] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
+      l_part += p[i];
+    }
+    const uint2 pt = make_uint2(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
+    // -- O^T += V^T P^T, V rows past the context zeroed (they may hold NaN)
+    uint32_t w[4][D / 64];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool live = tok0 + 4 * grp + e < t_end;
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) w[e][c] = live ? t.v[e][c] : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      // bytes j of the four rows' words, gathered per d-block db = 4c + j
+      const uint32_t a01 = perm_bytes(w[1][c], w[0][c], 0x05010400u);  // t0b0 t1b0 t0b1 t1b1
+      const uint32_t b01 = perm_bytes(w[1][c], w[0][c], 0x07030602u);  // t0b2 t1b2 t0b3 t1b3
+      const uint32_t a23 = perm_bytes(w[3][c], w[2][c], 0x05010400u);
+      const uint32_t b23 = perm_bytes(w[3][c], w[2][c], 0x07030602u);
+      const uint32_t xs[4] = {perm_bytes(a23, a01, 0x05040100u), perm_bytes(a23, a01, 0x07060302u),
+                              perm_bytes(b23, b01, 0x05040100u), perm_bytes(b23, b01, 0x07060302u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 vt = make_uint2(fp8x2_to_f16x2<false>(xs[j]), fp8x2_to_f16x2<true>(xs[j]));
+        const int b = 4 * c + j;
+        oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, vt),
+                                                        __builtin_bit_cast(f16x4_t, pt), oacc[b],
+                                                        0, 0, 0);
+      }
+    }
+  }
+
+  // l over the four lane groups (every lane of a head then holds it)
+  __device__ __forceinline__ void finish() {
+    l_part += xor_lanes(l_part, 16);
+    l_part += xor_lanes(l_part, 32);
+  }
+};
+
+// One work-group per (request, KV head, 16-head chunk[, partition]); wave w
+// takes every kMWaves-th block of the range.
+template <int D, bool PART>
+__global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a, int n_chunks) {
+  using Dec = MfmaDecoder<D>;
+  __shared__ MfmaDecodeSmem<D> sm;
+  const int r = blockIdx.z;
+  const int g = blockIdx.y / n_chunks;
+  const int hc = blockIdx.y - g * n_chunks;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h0 = g * G + hc * kMHeads;
+  const int nh = min(kMHeads, G - hc * kMHeads);
+
+  int row_q = r;
+  if (a.query_start_loc != nullptr) {
+    const int lo = a.query_start_loc[r];
+    if (a.query_start_loc[r + 1] - lo != 1) return;   // not a decode row
+    row_q = lo;
+  }
+  const int seq_len = a.seq_lens[r];
+  const int part = a.part_begin + (int)blockIdx.x;
+  int t_begin = 0, t_end = seq_len;
+  if constexpr (PART) {
+    t_begin = part * a.partition_size;
+    if (t_begin >= seq_len) return;
+    t_end = min(seq_len, t_begin + a.partition_size);
+  }
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+
+  if (t_end <= t_begin) {                           // empty context: zero row
+    if constexpr (!PART) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+      for (int i = tid; i < nh * D; i += kMWaves * kWave)
+        out[((int64_t)row_q * a.num_q_heads + h0 + i / D) * D + (i % D)] = 0;
+    }
+    return;
+  }
+
+  const float qk_scale = a.scale * kLog2e * *a.k_scale;
+  Dec dec;
+  dec.init(lane, qk_scale, a.alibi_slopes != nullptr);
+  dec.load_q(reinterpret_cast<const uint16_t*>(a.q), row_q, a.num_q_heads, h0, nh,
+             a.alibi_slopes, seq_len);
+  dec.reset();
+
+  const int first_block = t_begin / kBlock;
+  const int last_block = (t_end - 1) / kBlock;
+  const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+
+  for (int cb = first_block; cb <= last_block; cb += kMBtChunk) {
+    const int nb = min(last_block + 1 - cb, kMBtChunk);
+    __syncthreads();
+    for (int i = tid; i < nb; i += kMWaves * kWave) sm.bt[i] = bt_row[cb + i];
+    __syncthreads();
+    const int n = nb > w ? (nb - w + kMWaves - 1) / kMWaves : 0;
+    if (n > 0) {
+      // one tile in flight while the previous one is computed; the index of
+      // the prefetch is clamped so the load is unconditional
+      auto phys = [&](int it) {
+        return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * kMWaves]);
+      };
+      MTile<D> ta, tb;
+      mload<D>(ta, kbase, vbase, phys(0), g, a.num_kv_heads, lane);
+      for (int it = 0; it < n; it += 2) {
+        mload<D>(tb, kbase, vbase, phys(it + 1), g, a.num_kv_heads, lane);
+        dec.compute(ta, (cb + w + it * kMWaves) * kBlock, t_end);
+        if (it + 1 >= n) break;
+        mload<D>(ta, kbase, vbase, phys(it + 2), g, a.num_kv_heads, lane);
+        dec.compute(tb, (cb + w + (it + 1) * kMWaves) * kBlock, t_end);
+      }
+    }
+  }
+  dec.finish();
+  if (lane < kMHeads) {
+    sm.m[w][lane] = dec.m_run;
+    sm.mt[w][lane] = dec.m_true;
+    sm.l[w][lane] = dec.l_part;
+  }
+#pragma unroll
+  for (int b = 0; b < Dec::DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sm.acc[w][dec.col][(D / 4) * dec.grp + (D / 16) * i + b] = dec.oacc[b][i];
+  __syncthreads();
+
+  // ---- combine the waves and write (as decode_kernel)
+  const float vs = *a.v_scale;
+  for (int i = tid; i < kMHeads * D; i += kMWaves * kWave) {
+    const int j = i / D, dd = i - j * D;
+    if (j >= nh) continue;
+    float M = -INFINITY, Mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMWaves; ++u) {
+      M = fmaxf(M, sm.m[u][j]);
+      Mt = fmaxf(Mt, sm.mt[u][j]);
+    }
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMWaves; ++u) {
+      const float wgt = (sm.m[u][j] == -INFINITY) ? 0.f : fast_exp2(sm.m[u][j] - M);
+      L += sm.l[u][j] * wgt;
+      O += sm.acc[u][j][dd] * wgt;
+    }
+    O = O / L * vs;
+    const int h = h0 + j;
+    if constexpr (PART) {
+      const int64_t idx = ((int64_t)r * a.num_q_heads + h) * a.max_num_partitions + part;
+      a.tmp_out[idx * D + dd] = O;
+      if (dd == 0) {
+        a.max_logits[idx] = Mt * kLn2;
+        a.exp_sums[idx] = L * fast_exp2(M - Mt);
+      }
+    } else {
+      reinterpret_cast<uint16_t*>(a.out)[((int64_t)row_q * a.num_q_heads + h) * D + dd] =
+          f32_to_bf16(O);
+    }
+  }
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool partitioned, hipStream_t st) {
+  if (a.num_reqs == 0) return hipSuccess;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int n_chunks = (G + kMHeads - 1) / kMHeads;
+  dim3 grid(1, a.num_kv_heads * n_chunks, a.num_reqs);
+  if (partitioned) {
+    int nparts = (a.max_seq_len + a.partition_size - 1) / a.partition_size;
+    if (a.part_end > 0) nparts = min(nparts, a.part_end) - a.part_begin;
+    if (nparts <= 0) return hipSuccess;
+    grid.x = nparts;
+  }
+#define PA_MFMA(DV, PT) \
+  hipLaunchKernelGGL((decode_mfma_kernel<DV, PT>), grid, dim3(kMWaves * 64), 0, st, a, n_chunks)
+  if (a.head_dim == 64) {
+    if (partitioned) PA_MFMA(64, true); else PA_MFMA(64, false);
+  } else {
+    if (partitioned) PA_MFMA(128, true); else PA_MFMA(128, false);
+  }
+#undef PA_MFMA
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -67,6 +67,10 @@ hipError_t launch_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n,
 // request and KV head); true writes the partials.
 hipError_t launch_decode(const DecodeArgs& args, bool partitioned, hipStream_t stream);
 
+// FP8-cache decode on the matrix cores (same outputs and partials as
+// launch_decode); used by launch_decode for FP8 caches with G >= 4.
+hipError_t launch_decode_mfma(const DecodeArgs& args, bool partitioned, hipStream_t stream);
+
 // Work-balanced decode (output as launch_decode's single pass) and its
 // workspace size in bytes; at most balanced_max_reqs() requests.
 hipError_t launch_decode_balanced(const DecodeArgs& args, void* workspace, hipStream_t stream);
