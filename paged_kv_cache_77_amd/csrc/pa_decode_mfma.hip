@@ -8,7 +8,7 @@
 // 16-token block run as MFMAs with the GQA group's query heads on the N side
 // (16 per chunk; unused columns are zero queries):
 //
-//   S^T[16 tokens x 16 heads]  = K . Q^T   v_mfma_f32_16x16x32_bf16, D/32 steps;
+//   S^T[16 tokens x 16 heads]  = K . Q^T   v_mfma_f32_16x16x32_f16, D/32 steps;
 //       lane l supplies K row (token) l%16, d = (D/4)(l/16) + 8s .. +8 for step
 //       s, so its D/4 contiguous codes are one load; Q^T is permuted alike.
 //       The accumulator leaves lane l with tokens 4(l/16)+i of head l%16.
@@ -19,9 +19,10 @@
 //       The accumulator leaves lane l with d = (D/4)(l/16) + (D/16)i + db of
 //       head l%16 -- the same head as its softmax state.
 //
-// FP8 codes convert exactly to bf16 (K) and f16 (V); probabilities are f16
-// for the PV product (relative error <= 2^-11 per weight), l and the
-// max stay fp32.  Softmax in log2 units with the lazy running max of
+// FP8 codes convert exactly to f16; q enters as f16 after a per-head power
+// of two (exact for bf16 values in range, see load_q); probabilities are f16
+// for the PV product (relative error <= 2^-11 per weight), l and the max
+// stay fp32.  Softmax in log2 units with the lazy running max of
 // decode_kernel.
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -30,11 +31,16 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMHeads = 16;       // query heads per chunk (the MFMA N side)
 constexpr int kMWaves = 4;
 constexpr int kMBtChunk = 1024;
 constexpr float kMTau = 8.0f;
+#ifndef PA_MFMA_PREFETCH
+#define PA_MFMA_PREFETCH 3
+#endif
+constexpr int kMPrefetch = PA_MFMA_PREFETCH;   // tiles in flight per wave
 
 template <int D>
 struct MfmaDecodeSmem {
@@ -72,43 +78,64 @@ __device__ __forceinline__ void mload(MTile<D>& t, const uint8_t* kbase, const u
   }
 }
 
-template <int D>
+template <int D, bool ALIBI>
 struct MfmaDecoder {
   static constexpr int KS = D / 32;       // QK steps
   static constexpr int DB = D / 16;       // PV d-blocks
   int lane, col, grp;
-  bool has_alibi;
-  float qk_scale, alibi;
+  float qk_scale;                         // per lane: head col's scale (log2 units)
+  float alibi;
   int pos_q;
-  uint32_t qf[KS][4];                     // Q^T operand: 8 bf16 per step
+  uint32_t qf[KS][4];                     // Q^T operand: 8 f16 per step
   float m_run, m_true, l_part;            // head col (replicated in the 4 lane groups)
   f32x4_t oacc[DB];                       // MFMA accumulators, used in place
 
-  __device__ __forceinline__ void init(int lane_, float qk_scale_, bool has_alibi_) {
+  __device__ __forceinline__ void init(int lane_) {
     lane = lane_;
     col = lane % 16;
     grp = lane / 16;
-    qk_scale = qk_scale_;
-    has_alibi = has_alibi_;
     alibi = 0.f;
     pos_q = 0;
   }
 
-  // q of row row_q, heads h0 .. h0+nh-1 (column col; others zero)
+  // q of row row_q, heads h0 .. h0+nh-1 (column col; others zero), as f16
+  // scaled by a power of two 2^e per head (max |q| of the head lands in
+  // [2^14, 2^15), where f16 holds every bf16 value exactly; only elements
+  // below 2^-17 of the head's largest could round, far under the fp32
+  // rounding of the dot product).  The scores are scaled back by 2^-e.
   __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row_q, int num_q_heads,
-                                         int h0, int nh, const float* slopes, int seq_len) {
+                                         int h0, int nh, const float* slopes, int seq_len,
+                                         float scale_log2) {
     const bool real = col < nh;
     const uint16_t* qh = q + (row_q * num_q_heads + h0 + (real ? col : 0)) * D + (D / 4) * grp;
+    uint32_t raw[KS][4];
+    float amax = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * s);
-      qf[s][0] = real ? v.x : 0u;
-      qf[s][1] = real ? v.y : 0u;
-      qf[s][2] = real ? v.z : 0u;
-      qf[s][3] = real ? v.w : 0u;
+      raw[s][0] = real ? v.x : 0u;
+      raw[s][1] = real ? v.y : 0u;
+      raw[s][2] = real ? v.z : 0u;
+      raw[s][3] = real ? v.w : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16lo(raw[s][u])), fabsf(bf16hi(raw[s][u]))));
     }
+    amax = fmaxf(amax, xor_lanes(amax, 16));
+    amax = fmaxf(amax, xor_lanes(amax, 32));      // max |q| of head col
+    // exponent e with amax * 2^e in [2^14, 2^15); 0 for an all-zero head
+    int e = 0;
+    if (amax > 0.f && amax < INFINITY) e = 14 - (int)((__float_as_uint(amax) >> 23) & 0xff) + 127;
+    const float up = __uint_as_float((uint32_t)(127 + max(-126, min(127, e))) << 23);
+    const float down = __uint_as_float((uint32_t)(127 + max(-126, min(127, -e))) << 23);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        qf[s][u] = pack_f16x2(bf16lo(raw[s][u]) * up, bf16hi(raw[s][u]) * up);
+    qk_scale = scale_log2 * down;
     pos_q = seq_len - 1;
-    if (has_alibi) alibi = real ? slopes[h0 + col] * kLog2e : 0.f;
+    if constexpr (ALIBI) alibi = real ? slopes[h0 + col] * kLog2e : 0.f;
   }
 
   __device__ __forceinline__ void reset() {
@@ -120,29 +147,29 @@ struct MfmaDecoder {
   }
 
   __device__ __forceinline__ void compute(const MTile<D>& t, int tok0, int t_end) {
-    // -- S^T = K Q^T
+    // -- S^T = K Q^T (codes to exact f16 pairs)
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       const uint4 raw = t.k[st / 2];
       const uint32_t w0 = (st & 1) ? raw.z : raw.x;
       const uint32_t w1 = (st & 1) ? raw.w : raw.y;
-      const f32x4_t a = fp8x4_to_f32(w0), b = fp8x4_to_f32(w1);
-      const uint4 kb = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                                  pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+      const uint4 kb = make_uint4(fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0),
+                                  fp8x2_to_f16x2<false>(w1), fp8x2_to_f16x2<true>(w1));
       const uint4 qb = make_uint4(qf[st][0], qf[st][1], qf[st][2], qf[st][3]);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
-                                                  __builtin_bit_cast(bf16x8_t, qb), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, kb),
+                                                 __builtin_bit_cast(f16x8_t, qb), s, 0, 0, 0);
     }
-    // -- scaled scores of tokens tok0 + 4grp + i, masked by select
+    const bool full = tok0 + kBlock <= t_end;      // uniform
+    // -- scaled scores of tokens tok0 + 4grp + i (past the context: -inf)
     float x[4];
     float bm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + 4 * grp + i;
       float xv = s[i] * qk_scale;
-      if (has_alibi) xv = fmaf(alibi, (float)(tok - pos_q), xv);
-      x[i] = tok < t_end ? xv : -INFINITY;
+      if constexpr (ALIBI) xv = fmaf(alibi, (float)(tok - pos_q), xv);
+      x[i] = (full || tok < t_end) ? xv : -INFINITY;
       bm = fmaxf(bm, x[i]);
     }
     bm = fmaxf(bm, xor_lanes(bm, 16));
@@ -160,17 +187,24 @@ struct MfmaDecoder {
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_run);
+      p[i] = fast_exp2(x[i] - m_run);             // exp2(-inf) = 0 for masked tokens
       l_part += p[i];
     }
     const uint2 pt = make_uint2(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
-    // -- O^T += V^T P^T, V rows past the context zeroed (they may hold NaN)
+    // -- O^T += V^T P^T; in a partial block the rows past the context are
+    // zeroed (they may hold NaN, and 0 * NaN would poison the sum)
     uint32_t w[4][D / 64];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool live = tok0 + 4 * grp + e < t_end;
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) w[e][c] = live ? t.v[e][c] : 0u;
+      for (int c = 0; c < D / 64; ++c) w[e][c] = t.v[e][c];
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool live = tok0 + 4 * grp + e < t_end;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) w[e][c] = live ? w[e][c] : 0u;
+      }
     }
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
@@ -201,9 +235,9 @@ struct MfmaDecoder {
 
 // One work-group per (request, KV head, 16-head chunk[, partition]); wave w
 // takes every kMWaves-th block of the range.
-template <int D, bool PART>
+template <int D, bool PART, bool ALIBI>
 __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a, int n_chunks) {
-  using Dec = MfmaDecoder<D>;
+  using Dec = MfmaDecoder<D, ALIBI>;
   __shared__ MfmaDecodeSmem<D> sm;
   const int r = blockIdx.z;
   const int g = blockIdx.y / n_chunks;
@@ -239,11 +273,10 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a,
     return;
   }
 
-  const float qk_scale = a.scale * kLog2e * *a.k_scale;
   Dec dec;
-  dec.init(lane, qk_scale, a.alibi_slopes != nullptr);
+  dec.init(lane);
   dec.load_q(reinterpret_cast<const uint16_t*>(a.q), row_q, a.num_q_heads, h0, nh,
-             a.alibi_slopes, seq_len);
+             a.alibi_slopes, seq_len, a.scale * kLog2e * *a.k_scale);
   dec.reset();
 
   const int first_block = t_begin / kBlock;
@@ -259,19 +292,25 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a,
     __syncthreads();
     const int n = nb > w ? (nb - w + kMWaves - 1) / kMWaves : 0;
     if (n > 0) {
-      // one tile in flight while the previous one is computed; the index of
-      // the prefetch is clamped so the load is unconditional
+      // kMPrefetch tiles in flight while one is computed (a ring of
+      // registers, indices fixed by unrolling); the index of a prefetch is
+      // clamped so every load is unconditional
       auto phys = [&](int it) {
         return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * kMWaves]);
       };
-      MTile<D> ta, tb;
-      mload<D>(ta, kbase, vbase, phys(0), g, a.num_kv_heads, lane);
-      for (int it = 0; it < n; it += 2) {
-        mload<D>(tb, kbase, vbase, phys(it + 1), g, a.num_kv_heads, lane);
-        dec.compute(ta, (cb + w + it * kMWaves) * kBlock, t_end);
-        if (it + 1 >= n) break;
-        mload<D>(ta, kbase, vbase, phys(it + 2), g, a.num_kv_heads, lane);
-        dec.compute(tb, (cb + w + (it + 1) * kMWaves) * kBlock, t_end);
+      constexpr int NR = kMPrefetch + 1;
+      MTile<D> ring[NR];
+#pragma unroll
+      for (int j = 0; j < kMPrefetch; ++j)
+        mload<D>(ring[j], kbase, vbase, phys(j), g, a.num_kv_heads, lane);
+      for (int it = 0; it < n; it += NR) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          if (it + j >= n) break;
+          mload<D>(ring[(j + kMPrefetch) % NR], kbase, vbase, phys(it + j + kMPrefetch), g,
+                   a.num_kv_heads, lane);
+          dec.compute(ring[j], (cb + w + (it + j) * kMWaves) * kBlock, t_end);
+        }
       }
     }
   }
@@ -333,13 +372,16 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, bool partitioned, hipStream_t
     if (nparts <= 0) return hipSuccess;
     grid.x = nparts;
   }
-#define PA_MFMA(DV, PT) \
-  hipLaunchKernelGGL((decode_mfma_kernel<DV, PT>), grid, dim3(kMWaves * 64), 0, st, a, n_chunks)
+#define PA_MFMA(DV, PT, AL) \
+  hipLaunchKernelGGL((decode_mfma_kernel<DV, PT, AL>), grid, dim3(kMWaves * 64), 0, st, a, n_chunks)
+#define PA_MFMA_AL(DV, PT) \
+  do { if (a.alibi_slopes) PA_MFMA(DV, PT, true); else PA_MFMA(DV, PT, false); } while (0)
   if (a.head_dim == 64) {
-    if (partitioned) PA_MFMA(64, true); else PA_MFMA(64, false);
+    if (partitioned) PA_MFMA_AL(64, true); else PA_MFMA_AL(64, false);
   } else {
-    if (partitioned) PA_MFMA(128, true); else PA_MFMA(128, false);
+    if (partitioned) PA_MFMA_AL(128, true); else PA_MFMA_AL(128, false);
   }
+#undef PA_MFMA_AL
 #undef PA_MFMA
   return hipGetLastError();
 }
