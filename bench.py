@@ -50,7 +50,8 @@ DESCR = {
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_device.h", "pa_prefill.hip", "pa_cache_ops.hip"):
+    for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_device.h", "pa_prefill.hip",
+              "pa_cache_ops.hip", "pa_launch.h"):
         p = os.path.join(ROOT, "paged_kv_cache_77_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
@@ -65,8 +66,27 @@ def decode_bytes(w) -> dict:
     kv = int(ctx.sum()) * w.num_kv_heads * w.head_dim * 2 * eb
     qo = 2 * w.num_reqs * w.num_q_heads * w.head_dim * 2
     bt = 4 * int(((ctx + 15) // 16).sum())
+    # K/V bytes of the distinct physical blocks (a block shared by several
+    # requests counted once, with the most tokens any of them uses)
+    used = {}
+    for r in range(w.num_reqs):
+        n = int(ctx[r])
+        for j in range((n + 15) // 16):
+            b = int(w.block_table[r, j])
+            used[b] = max(used.get(b, 0), min(16, n - 16 * j))
+    kv_unique = sum(used.values()) * w.num_kv_heads * w.head_dim * 2 * eb
     return {"kv": kv, "q_o": qo, "table": bt + 4 * w.num_reqs, "tokens": int(ctx.sum()),
-            "total": kv + qo + bt + 4 * w.num_reqs}
+            "total": kv + qo + bt + 4 * w.num_reqs,
+            "unique_total": kv_unique + qo + bt + 4 * w.num_reqs}
+
+
+def decode_kernel_name(w) -> str:
+    """The kernel the library's decode dispatch runs for this shape: the
+    matrix-core kernel for FP8 caches with GQA groups of 4+ and bf16 caches
+    with groups of 8+ (pa_decode.hip, launch_any), else the vector-ALU one."""
+    G = w.num_q_heads // w.num_kv_heads
+    mfma = G >= 4 if w.cache_dtype == "fp8" else G >= 8
+    return "decode_mfma_kernel" if mfma else "decode_kernel"
 
 
 def traffic_for(kernel_key: str):
@@ -233,28 +253,41 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
         r["kbytes"] = nbytes["total"]
     elif path == "split":
         nparts = int(((w.seq_lens + P - 1) // P).sum())
-        r["kernel"] = f"decode_kernel (split-KV, P={P})"
+        r["kernel"] = f"{decode_kernel_name(w)} (split-KV, P={P})"
         r["kbytes"] = nbytes["total"] - nbytes["q_o"] // 2 + \
             nparts * w.num_q_heads * (w.head_dim + 2) * 4
     elif path == "balanced":
         r["kernel"] = "decode_balanced_kernel + balanced_merge_kernel"
         r["kbytes"] = nbytes["total"]
     else:
-        r["kernel"] = "decode_kernel (single pass)"
+        r["kernel"] = f"{decode_kernel_name(w)} (single pass)"
         r["kbytes"] = nbytes["total"]
     r["key"] = f"config{cfg}_{r['path']}"
+    if not is_prefill and nbytes["unique_total"] < nbytes["total"]:
+        # blocks shared between requests: HBM has to deliver each once, the
+        # re-reads come from L2 / the last-level cache.  The roofline takes
+        # the unique bytes; the per-request (served) bytes are reported too.
+        r["served_bytes"] = r["kbytes"]
+        r["kbytes"] = nbytes["unique_total"]
     if w.cache_dtype == "fp8" and not is_prefill:
-        # fp8 codes are decoded in registers and the shared prefix is served
-        # from cache, so the kernel's floor is the vector ALU: per (token, KV
-        # head) the method does G*d multiply-adds for q.k and G*d for p*v
-        # (2 flop each), issued as two-wide dot products
+        # per (token, KV head) the method does G*d multiply-adds for q.k and
+        # G*d for p*v (2 flop each): on the matrix cores (f16 operands) for
+        # the MFMA kernel, as two-wide vector dot products otherwise
         G = w.num_q_heads // w.num_kv_heads
         flops = 4 * G * w.head_dim * nbytes["tokens"] * w.num_kv_heads
         tf = flops / (kern_ms * 1e-3) / 1e12
-        r["alu"] = {"bound": "alu", "kernel": r["kernel"], "achieved": round(tf, 2),
-                    "peak": PEAK_VALU_DOT2_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / PEAK_VALU_DOT2_TFLOPS, 4),
-                    "algorithmic_flops_per_launch": flops}
+        if decode_kernel_name(w) == "decode_mfma_kernel":
+            r["alu"] = {"bound": "mfma", "kernel": r["kernel"], "achieved": round(tf, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "algorithmic_flops_per_launch": flops,
+                        "note": "f16 MFMA peak (= bf16); query heads padded to 16 per "
+                                "chunk on the MFMA N side are not counted"}
+        else:
+            r["alu"] = {"bound": "alu", "kernel": r["kernel"], "achieved": round(tf, 2),
+                        "peak": PEAK_VALU_DOT2_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_VALU_DOT2_TFLOPS, 4),
+                        "algorithmic_flops_per_launch": flops}
     del d, out, bufs, ws, sm
     torch.cuda.empty_cache()
     return r
@@ -266,7 +299,12 @@ def roofline_of(r) -> dict:
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic_for(r["key"]), "kernel_ms": round(r["kern_ms"], 5),
             "kernel_ms_stats": r["kernel_ms_stats"],
-            "algorithmic_bytes_per_launch": r["kbytes"]}
+            "algorithmic_bytes_per_launch": r["kbytes"],
+            **({"served_bytes_per_launch": r["served_bytes"],
+                "served_GBps": round(r["served_bytes"] / (r["kern_ms"] * 1e-3) / 1e9, 2),
+                "bytes_note": "achieved counts each shared block once (HBM's share); "
+                              "served counts every request's reads"}
+               if "served_bytes" in r else {})}
 
 
 def block_manager_rate() -> dict:
@@ -313,7 +351,7 @@ def summary(r) -> dict:
     if "prefill" in r:
         s["prefill_roofline"] = r["prefill"]
     if "alu" in r:
-        s["alu_roofline"] = r["alu"]
+        s["compute_roofline"] = r["alu"]
     return s
 
 
@@ -386,7 +424,7 @@ def main() -> int:
     if "prefill" in r:
         res["prefill_roofline"] = r["prefill"]
     if "alu" in r:
-        res["alu_roofline"] = r["alu"]
+        res["compute_roofline"] = r["alu"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
         res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)

@@ -72,6 +72,12 @@ constexpr int kLptMaxReqs = 128;
 #ifndef PA_DECODE_FP8_MFMA
 #define PA_DECODE_FP8_MFMA 1
 #endif
+// bf16 caches on the matrix cores from this GQA group size up (0: never).
+// Below it the vector-ALU kernel is as fast: its work per token grows with
+// the group, the matrix-core kernel's does not up to 16 heads.
+#ifndef PA_DECODE_BF16_MFMA_MIN_G
+#define PA_DECODE_BF16_MFMA_MIN_G 8
+#endif
 template <int GC, bool FP8, bool PART, int WAVES>
 constexpr int decode_min_waves() {
   return (!FP8 && !PART && GC <= 4 && WAVES == 8) ? PA_DECODE_MIN_WAVES_EU : 1;
@@ -1023,9 +1029,12 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int mode, void* ws, hipSt
 static hipError_t launch_any(const DecodeArgs& a, int mode, void* ws, hipStream_t st) {
   if (a.num_reqs == 0) return hipSuccess;
   const bool fp8 = a.cache_dtype != 0;
-  // FP8 caches with groups of 4+ query heads: the MFMA kernel (the vector-ALU
-  // kernel is the limit there, not memory)
+  // FP8 caches with groups of 4+ query heads, bf16 ones with large groups:
+  // the MFMA kernel (the vector-ALU kernel is the limit there, not memory)
   if (PA_DECODE_FP8_MFMA && fp8 && mode != 2 && a.num_q_heads / a.num_kv_heads >= 4)
+    return launch_decode_mfma(a, mode == 1, st);
+  if (PA_DECODE_BF16_MFMA_MIN_G > 0 && !fp8 && mode != 2 &&
+      a.num_q_heads / a.num_kv_heads >= PA_DECODE_BF16_MFMA_MIN_G)
     return launch_decode_mfma(a, mode == 1, st);
   if (a.head_dim == 64)
     return fp8 ? launch_decode_d<64, true>(a, mode, ws, st)

@@ -1,29 +1,33 @@
-// FP8-cache paged decode on the matrix cores (gfx950).
+// Paged decode on the matrix cores (gfx950): FP8 caches, and bf16 caches
+// with large GQA groups.
 //
 // Same result as decode_kernel ("vLLM 深度解析（二）：PagedAttention 核心机制"
 // §3.2: block-table walk, scaled q.k of the query heads sharing a KV head,
 // masked tail, softmax, PV; §2.2: the running (m, l, A) state; §3.2.7 for the
-// split-KV partials).  With an FP8 cache the shared-prefix workloads are not
-// memory-bound -- the vector ALU was the limit -- so the two products of a
-// 16-token block run as MFMAs with the GQA group's query heads on the N side
-// (16 per chunk; unused columns are zero queries):
+// split-KV partials).  Where the vector ALU, not memory, is the limit (FP8
+// caches: four conversions per code; bf16 caches: work per token that grows
+// with the group) the two products of a 16-token block run as MFMAs with the
+// GQA group's query heads on the N side (16 per chunk; unused columns are
+// zero queries):
 //
-//   S^T[16 tokens x 16 heads]  = K . Q^T   v_mfma_f32_16x16x32_f16, D/32 steps;
-//       lane l supplies K row (token) l%16, d = (D/4)(l/16) + 8s .. +8 for step
-//       s, so its D/4 contiguous codes are one load; Q^T is permuted alike.
-//       The accumulator leaves lane l with tokens 4(l/16)+i of head l%16.
-//   O^T[D x 16 heads] += V^T . P^T          v_mfma_f32_16x16x16_f16, D/16 steps;
-//       P^T is the lane's own four probabilities (f16), V^T row m of d-block
-//       db is d = (D/16)m + db, so lane l loads D/16 contiguous codes of each
-//       of its four tokens and byte-shuffles them into f16 pairs (exact).
-//       The accumulator leaves lane l with d = (D/4)(l/16) + (D/16)i + db of
-//       head l%16 -- the same head as its softmax state.
+//   S^T[16 tokens x 16 heads]  = K . Q^T   v_mfma_f32_16x16x32_{f16,bf16},
+//       D/32 steps; lane l supplies K row (token) l%16, d = (D/4)(l/16) + 8s
+//       .. +8 for step s, so its D/4 contiguous elements are one load; Q^T
+//       is permuted alike.  The accumulator leaves lane l with tokens
+//       4(l/16)+i of head l%16.
+//   O^T[D x 16 heads] += V^T . P^T          v_mfma_f32_16x16x16_{f16,bf16},
+//       D/16 steps; P^T is the lane's own four probabilities, V^T row m of
+//       d-block db is d = (D/16)m + db, so lane l loads D/16 contiguous
+//       elements of each of its four tokens and shuffles them into pairs
+//       (exact).  The accumulator leaves lane l with d = (D/4)(l/16) +
+//       (D/16)i + db of head l%16 -- the same head as its softmax state.
 //
-// FP8 codes convert exactly to f16; q enters as f16 after a per-head power
+// FP8: codes convert exactly to f16; q enters as f16 after a per-head power
 // of two (exact for bf16 values in range, see load_q); probabilities are f16
-// for the PV product (relative error <= 2^-11 per weight), l and the max
-// stay fp32.  Softmax in log2 units with the lazy running max of
-// decode_kernel.
+// for the PV product (relative error <= 2^-11 per weight).  bf16: K, V and q
+// enter unchanged; probabilities are split into two bf16 terms (about 16
+// significant bits).  l and the max stay fp32; softmax in log2 units with
+// the lazy running max of decode_kernel.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -32,15 +36,30 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMHeads = 16;       // query heads per chunk (the MFMA N side)
-constexpr int kMWaves = 4;
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
+constexpr int kMWaves = PA_MFMA_WAVES;
+#ifndef PA_MFMA_LPT_MAX
+#define PA_MFMA_LPT_MAX 128
+#endif
+constexpr int kMaxLptReqs = PA_MFMA_LPT_MAX;   // longest-first order up to this batch
 constexpr int kMBtChunk = 1024;
 constexpr float kMTau = 8.0f;
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 3
 #endif
 constexpr int kMPrefetch = PA_MFMA_PREFETCH;   // tiles in flight per wave
+#ifndef PA_MFMA_PREFETCH_BF16
+#define PA_MFMA_PREFETCH_BF16 2
+#endif
+constexpr int kMPrefetchB = PA_MFMA_PREFETCH_BF16;   // bf16 tiles are twice the bytes
+#ifndef PA_MFMA_MINW_BF16
+#define PA_MFMA_MINW_BF16 1
+#endif
 
 template <int D>
 struct MfmaDecodeSmem {
@@ -49,6 +68,7 @@ struct MfmaDecodeSmem {
   float mt[kMWaves][kMHeads];
   float l[kMWaves][kMHeads];
   float acc[kMWaves][kMHeads][D];
+  int32_t sched;
 };
 
 template <int D>
@@ -233,13 +253,214 @@ struct MfmaDecoder {
   }
 };
 
+// ---------------------------------------------------------------------------
+// bf16 caches: the same two products with bf16 operands.  K rows need no
+// conversion; V^T pairs are 16-bit shuffles; P^T is split into a bf16 high
+// part and a bf16 remainder (two MFMAs), so the probabilities keep ~16
+// significant bits -- bf16 alone (8 bits) would cost more accuracy than the
+// output's own rounding allows on peaked softmaxes.
+template <int D>
+struct MTileB {
+  uint4 k[D / 32];               // D/4 bf16 of one K row (8 per step)
+  uint32_t v[4][D / 32];         // D/16 bf16 of each of four V rows
+};
+
+template <int D>
+__device__ __forceinline__ void mloadB(MTileB<D>& t, const uint8_t* kbase, const uint8_t* vbase,
+                                       int32_t phys, int g, int num_kv_heads, int lane) {
+  const int64_t off = tile_offset(phys, g, num_kv_heads, D) * 2;     // bytes
+  const int row = lane % 16, grp = lane / 16;
+  const uint8_t* kp = kbase + off + (row * D + (D / 4) * grp) * 2;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + 16 * c);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint8_t* vp = vbase + off + ((4 * grp + e) * D + (D / 16) * row) * 2;
+    if constexpr (D / 32 == 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(vp);
+      t.v[e][0] = w.x; t.v[e][1] = w.y; t.v[e][2] = w.z; t.v[e][3] = w.w;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(vp);
+      t.v[e][0] = w.x; t.v[e][1] = w.y;
+    }
+  }
+}
+
+template <int D, bool ALIBI>
+struct MfmaDecoderB {
+  static constexpr int KS = D / 32;
+  static constexpr int DB = D / 16;
+  int lane, col, grp;
+  float qk_scale, alibi;
+  int pos_q;
+  uint32_t qf[KS][4];
+  float m_run, m_true, l_part;
+  f32x4_t oacc[DB];
+
+  __device__ __forceinline__ void init(int lane_) {
+    lane = lane_;
+    col = lane % 16;
+    grp = lane / 16;
+    alibi = 0.f;
+    pos_q = 0;
+  }
+
+  __device__ __forceinline__ void load_q(const uint16_t* q, int64_t row_q, int num_q_heads,
+                                         int h0, int nh, const float* slopes, int seq_len,
+                                         float scale_log2) {
+    const bool real = col < nh;
+    const uint16_t* qh = q + (row_q * num_q_heads + h0 + (real ? col : 0)) * D + (D / 4) * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * s);
+      qf[s][0] = real ? v.x : 0u;
+      qf[s][1] = real ? v.y : 0u;
+      qf[s][2] = real ? v.z : 0u;
+      qf[s][3] = real ? v.w : 0u;
+    }
+    qk_scale = scale_log2;
+    pos_q = seq_len - 1;
+    if constexpr (ALIBI) alibi = real ? slopes[h0 + col] * kLog2e : 0.f;
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    m_true = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) oacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ __forceinline__ void compute(const MTileB<D>& t, int tok0, int t_end) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const uint4 qb = make_uint4(qf[st][0], qf[st][1], qf[st][2], qf[st][3]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[st]),
+                                                  __builtin_bit_cast(bf16x8_t, qb), s, 0, 0, 0);
+    }
+    const bool full = tok0 + kBlock <= t_end;
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + 4 * grp + i;
+      float xv = s[i] * qk_scale;
+      if constexpr (ALIBI) xv = fmaf(alibi, (float)(tok - pos_q), xv);
+      x[i] = (full || tok < t_end) ? xv : -INFINITY;
+      bm = fmaxf(bm, x[i]);
+    }
+    bm = fmaxf(bm, xor_lanes(bm, 16));
+    bm = fmaxf(bm, xor_lanes(bm, 32));
+    m_true = fmaxf(m_true, bm);
+    const bool grow = bm > m_run + kMTau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? bm : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) oacc[b] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - m_run);
+      l_part += p[i];
+    }
+    // P^T = high + remainder, both bf16
+    const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l01 = pack_bf16x2(p[0] - bf16lo(h01), p[1] - bf16hi(h01));
+    const uint32_t l23 = pack_bf16x2(p[2] - bf16lo(h23), p[3] - bf16hi(h23));
+    const uint2 ph = make_uint2(h01, h23), pl = make_uint2(l01, l23);
+    uint32_t w[4][D / 32];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) w[e][c] = t.v[e][c];
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool live = tok0 + 4 * grp + e < t_end;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) w[e][c] = live ? w[e][c] : 0u;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      // element b of the four rows: 16-bit half b%2 of word b/2
+      const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+      const uint2 vt = make_uint2(perm_bytes(w[1][b / 2], w[0][b / 2], sel),
+                                  perm_bytes(w[3][b / 2], w[2][b / 2], sel));
+      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, vt),
+                                                          __builtin_bit_cast(bf16x4_t, ph),
+                                                          oacc[b], 0, 0, 0);
+      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, vt),
+                                                          __builtin_bit_cast(bf16x4_t, pl),
+                                                          oacc[b], 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void finish() {
+    l_part += xor_lanes(l_part, 16);
+    l_part += xor_lanes(l_part, 32);
+  }
+};
+
+// Path selection for the kernel: tile type, loader, decoder, cache scales.
+template <int D, bool ALIBI, bool FP8>
+struct MPath;
+template <int D, bool ALIBI>
+struct MPath<D, ALIBI, true> {
+  using Tile = MTile<D>;
+  using Dec = MfmaDecoder<D, ALIBI>;
+  static constexpr int kPrefetch = kMPrefetch;
+  static __device__ __forceinline__ void load(Tile& t, const uint8_t* kb, const uint8_t* vb,
+                                              int32_t phys, int g, int hkv, int lane) {
+    mload<D>(t, kb, vb, phys, g, hkv, lane);
+  }
+};
+template <int D, bool ALIBI>
+struct MPath<D, ALIBI, false> {
+  using Tile = MTileB<D>;
+  using Dec = MfmaDecoderB<D, ALIBI>;
+  static constexpr int kPrefetch = kMPrefetchB;
+  static __device__ __forceinline__ void load(Tile& t, const uint8_t* kb, const uint8_t* vb,
+                                              int32_t phys, int g, int hkv, int lane) {
+    mloadB<D>(t, kb, vb, phys, g, hkv, lane);
+  }
+};
+
 // One work-group per (request, KV head, 16-head chunk[, partition]); wave w
 // takes every kMWaves-th block of the range.
-template <int D, bool PART, bool ALIBI>
-__global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a, int n_chunks) {
-  using Dec = MfmaDecoder<D, ALIBI>;
+template <int D, bool PART, bool ALIBI, bool FP8>
+__global__ __launch_bounds__(kMWaves * 64, FP8 ? 1 : PA_MFMA_MINW_BF16) void decode_mfma_kernel(
+    DecodeArgs a, int n_chunks) {
+  using Path = MPath<D, ALIBI, FP8>;
+  using Dec = typename Path::Dec;
   __shared__ MfmaDecodeSmem<D> sm;
-  const int r = blockIdx.z;
+  // With a.lpt, blockIdx.z is a rank: the request with the rank-th longest
+  // context (ties by index), so the longest units are handed out first.
+  int r = blockIdx.z;
+  if constexpr (!PART) {
+    if (a.lpt) {
+      const int R = a.num_reqs;
+      for (int i = threadIdx.x; i < R; i += kMWaves * kWave) sm.bt[i] = a.seq_lens[i];
+      __syncthreads();
+      for (int j = threadIdx.x; j < R; j += kMWaves * kWave) {
+        const int lj = sm.bt[j];
+        int rank = 0;
+        for (int k = 0; k < R; ++k) {
+          const int lk = sm.bt[k];
+          rank += (lk > lj || (lk == lj && k < j)) ? 1 : 0;
+        }
+        if (rank == (int)blockIdx.z) sm.sched = j;
+      }
+      __syncthreads();
+      r = __builtin_amdgcn_readfirstlane(sm.sched);
+      __syncthreads();
+    }
+  }
   const int g = blockIdx.y / n_chunks;
   const int hc = blockIdx.y - g * n_chunks;
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -276,7 +497,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a,
   Dec dec;
   dec.init(lane);
   dec.load_q(reinterpret_cast<const uint16_t*>(a.q), row_q, a.num_q_heads, h0, nh,
-             a.alibi_slopes, seq_len, a.scale * kLog2e * *a.k_scale);
+             a.alibi_slopes, seq_len, a.scale * kLog2e * (FP8 ? *a.k_scale : 1.f));
   dec.reset();
 
   const int first_block = t_begin / kBlock;
@@ -292,23 +513,24 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a,
     __syncthreads();
     const int n = nb > w ? (nb - w + kMWaves - 1) / kMWaves : 0;
     if (n > 0) {
-      // kMPrefetch tiles in flight while one is computed (a ring of
+      // PF tiles in flight while one is computed (a ring of
       // registers, indices fixed by unrolling); the index of a prefetch is
       // clamped so every load is unconditional
       auto phys = [&](int it) {
         return __builtin_amdgcn_readfirstlane(sm.bt[w + min(it, n - 1) * kMWaves]);
       };
-      constexpr int NR = kMPrefetch + 1;
-      MTile<D> ring[NR];
+      constexpr int PF = Path::kPrefetch;
+      constexpr int NR = PF + 1;
+      typename Path::Tile ring[NR];
 #pragma unroll
-      for (int j = 0; j < kMPrefetch; ++j)
-        mload<D>(ring[j], kbase, vbase, phys(j), g, a.num_kv_heads, lane);
+      for (int j = 0; j < PF; ++j)
+        Path::load(ring[j], kbase, vbase, phys(j), g, a.num_kv_heads, lane);
       for (int it = 0; it < n; it += NR) {
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
           if (it + j >= n) break;
-          mload<D>(ring[(j + kMPrefetch) % NR], kbase, vbase, phys(it + j + kMPrefetch), g,
-                   a.num_kv_heads, lane);
+          Path::load(ring[(j + PF) % NR], kbase, vbase, phys(it + j + PF), g,
+                     a.num_kv_heads, lane);
           dec.compute(ring[j], (cb + w + (it + j) * kMWaves) * kBlock, t_end);
         }
       }
@@ -328,7 +550,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_mfma_kernel(DecodeArgs a,
   __syncthreads();
 
   // ---- combine the waves and write (as decode_kernel)
-  const float vs = *a.v_scale;
+  const float vs = FP8 ? *a.v_scale : 1.f;
   for (int i = tid; i < kMHeads * D; i += kMWaves * kWave) {
     const int j = i / D, dd = i - j * D;
     if (j >= nh) continue;
@@ -372,8 +594,21 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, bool partitioned, hipStream_t
     if (nparts <= 0) return hipSuccess;
     grid.x = nparts;
   }
+  const bool fp8 = a.cache_dtype != 0;
+  DecodeArgs b = a;
+  // (rank search: O(num_reqs) per thread, so modest batches only; the
+  // rank buffer is the block-table staging array)
+  static_assert(kMaxLptReqs <= kMBtChunk, "rank buffer");
+  b.lpt = (!partitioned && a.query_start_loc == nullptr && a.num_reqs <= kMaxLptReqs) ? 1 : 0;
 #define PA_MFMA(DV, PT, AL) \
-  hipLaunchKernelGGL((decode_mfma_kernel<DV, PT, AL>), grid, dim3(kMWaves * 64), 0, st, a, n_chunks)
+  do {                                                                                        \
+    if (fp8)                                                                                  \
+      hipLaunchKernelGGL((decode_mfma_kernel<DV, PT, AL, true>), grid, dim3(kMWaves * 64), 0, \
+                         st, b, n_chunks);                                                    \
+    else                                                                                      \
+      hipLaunchKernelGGL((decode_mfma_kernel<DV, PT, AL, false>), grid, dim3(kMWaves * 64), 0, \
+                         st, b, n_chunks);                                                    \
+  } while (0)
 #define PA_MFMA_AL(DV, PT) \
   do { if (a.alibi_slopes) PA_MFMA(DV, PT, true); else PA_MFMA(DV, PT, false); } while (0)
   if (a.head_dim == 64) {

@@ -58,7 +58,7 @@ RUNS = {
         "title": "shared-prefix fp8 decode: 256 requests sharing 256 blocks (4096 tokens) + "
                  "tails U[64,1024], 28 q / 4 KV heads, head_dim 128, fp8 e4m3 K/V",
         "args": "--config 5",
-        "keys": {"config5_single": ["pa::decode_kernel"]},
+        "keys": {"config5_single": ["pa::decode_mfma_kernel"]},
     },
 }
 
@@ -178,7 +178,11 @@ def summarize(outdir: str = "gpurun_out/prof", profiles: str = "profiles") -> di
             lines.append(f"# bench.py (same run, HIP events): kernel {rl['kernel_ms'] * 1e3:.3f} us, "
                          f"algorithmic {rl['algorithmic_bytes_per_launch'] / 1e6:.2f} MB/launch, "
                          f"{rl['achieved']:.1f} GB/s = {rl['frac']:.4f} of {rl['peak']:.0f}")
-            for extra in ("prefill_roofline", "alu_roofline"):
+            if "served_GBps" in rl:
+                lines.append(f"# bench.py: served (every request's reads) "
+                             f"{rl['served_bytes_per_launch'] / 1e6:.2f} MB/launch, "
+                             f"{rl['served_GBps']:.1f} GB/s")
+            for extra in ("prefill_roofline", "compute_roofline"):
                 if extra in bench_line:
                     e = bench_line[extra]
                     lines.append(f"# bench.py {extra}: {e['achieved']} {e['unit']} = "

@@ -48,6 +48,8 @@ SHAPES = [
     (4, 2, 64, "bf16"), (32, 8, 128, "bf16"), (8, 8, 128, "bf16"), (6, 2, 128, "bf16"),
     (28, 4, 128, "bf16"), (16, 2, 64, "bf16"), (32, 2, 128, "bf16"),
     (28, 4, 128, "fp8"), (8, 2, 128, "fp8"), (4, 4, 64, "fp8"), (16, 2, 64, "fp8"),
+    # groups over 16 heads: a full and a partial 16-head chunk
+    (48, 2, 128, "bf16"), (40, 2, 64, "fp8"),
 ]
 CTX = [1, 15, 16, 17, 63, 64, 65, 130, 1000, 2049]
 
@@ -207,7 +209,8 @@ def test_balanced_workspace_reuse_and_all_units_written():
 
 
 @pytest.mark.parametrize("hq,hkv,d,cache", [(32, 8, 128, "bf16"), (28, 4, 128, "fp8"),
-                                            (4, 2, 64, "bf16"), (16, 2, 64, "fp8")])
+                                            (4, 2, 64, "bf16"), (16, 2, 64, "fp8"),
+                                            (16, 2, 128, "bf16")])
 def test_decode_alibi_all_paths(hq, hkv, d, cache):
     """ALiBi slopes 2^(-8(h+1)/Hq): single pass, balanced and split-KV (with
     the partials) against the oracle."""
