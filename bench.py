@@ -195,18 +195,22 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     warm = sorted(a.elapsed_time(b) for a, b in ev)
     kern_ms = sum(warm) / len(warm)
 
-    # cold-cache timing of the same kernel(s): a 1 GiB write between
-    # launches evicts L2 and the 256 MB Infinity Cache (MALL)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    # cold-cache timing of the same kernel(s): reading 1 GiB between
+    # launches evicts L2 and the 256 MB Infinity Cache (MALL).  A read, not
+    # a write: dirty flush lines would be written back inside the timed
+    # kernel and charge it for traffic that is not its own.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = flush.sum()
+    torch.cuda.synchronize()
     cold_ev = []
     for _ in range(cold_reps):
-        flush.fill_(1.0)
+        sink = flush.sum()
         n0 = len(ev)
         step(True)
         cold_ev.append(ev[n0])
     torch.cuda.synchronize()
     cold = sorted(a.elapsed_time(b) for a, b in cold_ev)
-    del flush
+    del flush, sink
 
     def pct(v, q):
         return round(v[min(len(v) - 1, int(q * len(v)))], 5)
@@ -217,7 +221,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
              "warm": {"median": pct(warm, 0.5), "p10": pct(warm, 0.1), "p90": pct(warm, 0.9),
                       "reps": len(warm)},
              "cold": ({"median": pct(cold, 0.5), "p10": pct(cold, 0.1), "p90": pct(cold, 0.9),
-                       "reps": len(cold), "flush": "1 GiB device write before each launch"}
+                       "reps": len(cold), "flush": "1 GiB device read before each launch"}
                       if cold else None)}}
 
     if is_prefill:

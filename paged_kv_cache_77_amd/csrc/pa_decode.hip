@@ -68,6 +68,11 @@ constexpr float kTau = 8.0f;
 #define PA_DECODE_LPT 1
 #endif
 constexpr int kLptMaxReqs = 128;
+// Streaming (non-temporal) K/V loads for bf16 caches (FP8 ones are the
+// shared-prefix case, which lives on L2 hits).
+#ifndef PA_DECODE_NT_BF16
+#define PA_DECODE_NT_BF16 1
+#endif
 // FP8 decode on the matrix cores for G >= 4 (0: always the vector-ALU kernel).
 #ifndef PA_DECODE_FP8_MFMA
 #define PA_DECODE_FP8_MFMA 1
@@ -107,10 +112,22 @@ struct Words {
   uint32_t w[N];
 };
 
-template <int N>
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// NT: non-temporal (streaming) loads, for data that is read once
+template <int N, bool NT = false>
 __device__ __forceinline__ Words<N> load_words(const uint8_t* p) {
   Words<N> r;
-  if constexpr (N == 4) {
+  if constexpr (NT && N == 4) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NT && N == 2) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (NT) {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  } else if constexpr (N == 4) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (N == 2) {
@@ -134,6 +151,7 @@ struct WaveDecoder {
   using S = DecodeShape<D, GC, FP8>;
   static constexpr int EB = S::EB, LPR = S::LPR, RK = S::RK, KCH = S::KCH, KW = S::KW,
                        KCHB = S::KCHB, QW = S::QW, VE = S::VE, VW = S::VW, GCP = S::GCP;
+  static constexpr bool kStream = PA_DECODE_NT_BF16 && !FP8;
   struct Tile {
     Words<KW> k[RK][KCH];
     Words<VW> v[4];
@@ -207,11 +225,11 @@ struct WaveDecoder {
     for (int i = 0; i < RK; ++i)
 #pragma unroll
       for (int k = 0; k < KCH; ++k)
-        t.k[i][k] = load_words<KW>(kt + (krow0 + (64 / LPR) * i) * (D * EB) +
-                                   (kc + LPR * k) * KCHB);
+        t.k[i][k] = load_words<KW, kStream>(kt + (krow0 + (64 / LPR) * i) * (D * EB) +
+                                            (kc + LPR * k) * KCHB);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      t.v[i] = load_words<VW>(vt + ((vrg + 4 * i) * D + vcol) * EB);
+      t.v[i] = load_words<VW, kStream>(vt + ((vrg + 4 * i) * D + vcol) * EB);
   }
 
   // Fold one block (tokens tok0 .. tok0+15, those >= t_end excluded) into

@@ -265,6 +265,8 @@ struct MTileB {
   uint32_t v[4][D / 32];         // D/16 bf16 of each of four V rows
 };
 
+// (plain loads: each load instruction covers part of every cache line of
+// the tile, so streaming loads, which do not keep the line, re-fetch it)
 template <int D>
 __device__ __forceinline__ void mloadB(MTileB<D>& t, const uint8_t* kbase, const uint8_t* vbase,
                                        int32_t phys, int g, int num_kv_heads, int lane) {
