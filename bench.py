@@ -285,8 +285,11 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "algorithmic_flops_per_launch": flops,
+                        "vs_vector_alu_peak": round(tf / PEAK_VALU_DOT2_TFLOPS, 4),
                         "note": "f16 MFMA peak (= bf16); query heads padded to 16 per "
-                                "chunk on the MFMA N side are not counted"}
+                                "chunk on the MFMA N side are not counted; "
+                                "vs_vector_alu_peak: the same flops against the vector "
+                                "ALU's dot2 peak (the bound of the vector kernel)"}
         else:
             r["alu"] = {"bound": "alu", "kernel": r["kernel"], "achieved": round(tf, 2),
                         "peak": PEAK_VALU_DOT2_TFLOPS, "unit": "TFLOP/s",
