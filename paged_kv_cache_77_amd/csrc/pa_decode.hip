@@ -49,6 +49,13 @@ constexpr float kTau = 8.0f;
 #ifndef PA_DECODE_WAVES_SINGLE
 #define PA_DECODE_WAVES_SINGLE 8
 #endif
+// ... and only for contexts long enough to give the extra waves blocks:
+// max_seq_len >= this, twice this from 384 work-groups on (measured on
+// MI355X: at 512 groups and 256..1024-token contexts 4 waves are up to 30%
+// faster; with few groups 8 waves win from 1024 tokens).
+#ifndef PA_DECODE_WAVES_SINGLE_MIN_LEN
+#define PA_DECODE_WAVES_SINGLE_MIN_LEN 1024
+#endif
 #ifndef PA_DECODE_WAVES_SPLIT
 #define PA_DECODE_WAVES_SPLIT 4
 #endif
@@ -980,7 +987,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     DecodeArgs b = a;
     // (the rank search costs O(num_reqs) per thread: kept to modest batches)
     b.lpt = (PA_DECODE_LPT && a.query_start_loc == nullptr && a.num_reqs <= kLptMaxReqs) ? 1 : 0;
-    if (groups < 768) {
+    const int64_t min_len = groups < 384 ? PA_DECODE_WAVES_SINGLE_MIN_LEN
+                                         : 2 * PA_DECODE_WAVES_SINGLE_MIN_LEN;
+    if (groups < 768 && a.max_seq_len >= min_len) {
       constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
       hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,
                          st, b, n_chunks);

@@ -107,6 +107,25 @@ def test_decode_long_single_pass_and_boosted_rows():
     check_bf16(dv.bits_of(out3), ref, "balanced")
 
 
+@pytest.mark.parametrize("ctx_hi,cache", [(700, "bf16"), (1900, "bf16"), (1900, "fp8")])
+def test_decode_wide_batch_both_wave_counts(ctx_hi, cache):
+    """64 requests x 8 KV heads (512 work-groups): contexts up to 700 take the
+    4-wave single pass, up to 1900 with a 1900-token request too; the fp8
+    case runs the matrix-core kernel with longest-first order."""
+    _announce(f"decode wide batch ctx<= {ctx_hi} {cache}")
+    rng = np.random.default_rng(ctx_hi)
+    ctx = [int(x) for x in rng.integers(1, ctx_hi + 1, size=64)]
+    ctx[5] = ctx_hi
+    w = wl.make_workload(name="t", seq_lens=ctx, q_lens=[1] * 64, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, seed=36 + ctx_hi, cache_dtype=cache,
+                         writes_new_kv=False)
+    d = dv.to_device(w)
+    out = _out(w)
+    dv.run_decode(d, out)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(out), oracle.decode(w), "pa_decode")
+
+
 def test_decode_empty_context_is_zero():
     _announce("decode seq_len 0")
     w = wl.make_workload(name="t", seq_lens=[0, 20], q_lens=[0, 0], num_q_heads=4,
