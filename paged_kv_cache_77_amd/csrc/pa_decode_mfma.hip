@@ -50,7 +50,7 @@ constexpr int kMaxLptReqs = PA_MFMA_LPT_MAX;   // longest-first order up to this
 constexpr int kMBtChunk = 1024;
 constexpr float kMTau = 8.0f;
 #ifndef PA_MFMA_PREFETCH
-#define PA_MFMA_PREFETCH 3
+#define PA_MFMA_PREFETCH 2
 #endif
 constexpr int kMPrefetch = PA_MFMA_PREFETCH;   // tiles in flight per wave
 #ifndef PA_MFMA_PREFETCH_BF16
@@ -59,6 +59,13 @@ constexpr int kMPrefetch = PA_MFMA_PREFETCH;   // tiles in flight per wave
 constexpr int kMPrefetchB = PA_MFMA_PREFETCH_BF16;   // bf16 tiles are twice the bytes
 #ifndef PA_MFMA_MINW_BF16
 #define PA_MFMA_MINW_BF16 1
+#endif
+// FP8 work-groups fit 4 per CU at 128 VGPRs with 2 tiles in flight (the
+// whole shared-prefix grid resident at once: 4% faster than 3 per CU with a
+// 3-tile ring; a 3-tile ring at 128 VGPRs spills, and so would ALiBi, which
+// gets 3 per CU)
+#ifndef PA_MFMA_MINW_FP8
+#define PA_MFMA_MINW_FP8 4
 #endif
 
 template <int D>
@@ -436,7 +443,7 @@ struct MPath<D, ALIBI, false> {
 // One work-group per (request, KV head, 16-head chunk[, partition]); wave w
 // takes every kMWaves-th block of the range.
 template <int D, bool PART, bool ALIBI, bool FP8>
-__global__ __launch_bounds__(kMWaves * 64, FP8 ? 1 : PA_MFMA_MINW_BF16) void decode_mfma_kernel(
+__global__ __launch_bounds__(kMWaves * 64, FP8 ? (ALIBI ? 3 : PA_MFMA_MINW_FP8) : PA_MFMA_MINW_BF16) void decode_mfma_kernel(
     DecodeArgs a, int n_chunks) {
   using Path = MPath<D, ALIBI, FP8>;
   using Dec = typename Path::Dec;
