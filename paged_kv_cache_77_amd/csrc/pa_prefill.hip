@@ -23,10 +23,13 @@
 //       accumulators: the MFMA contraction order over keys is permuted to the
 //       order the accumulators hold them, and V^T is stored in LDS in that
 //       order)
-// K is staged row-major with a 16-byte-chunk XOR swizzle, V transposed
-// (d-major) with the key permutation and a swizzle on d >> 1 (rows of V^T are
-// 128 bytes, so two consecutive rows share a 256-byte bank line); both
-// double-buffered.
+// bf16 caches: each wave copies one 16-token block of K and of V straight
+// from global memory into LDS (global_load_lds_dwordx4: no staging
+// registers), both row-major with a 16-byte-chunk XOR swizzle; the V^T
+// fragments of the PV products come from gfx950's transposing LDS read
+// (ds_read_b64_tr_b16).  FP8 caches are converted to bf16 in registers on
+// the way: K is stored as above, V transposed (d-major) with the key
+// permutation and a swizzle on d >> 1.  All tiles are double-buffered.
 #include <algorithm>
 
 #include "pa_device.h"
@@ -36,6 +39,22 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// LDS offset of a generic pointer to an LDS object (its low 32 bits)
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// v_mfma / ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane
+// i receives element i % 4 of the 64-bit values addressed by lanes
+// 4e + i / 4, e = 0..3 (a 4 x 4 transpose of 16-bit elements per group).
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
 
 constexpr int kBN = 64;         // keys per tile
 constexpr int kWaves = 4;
@@ -186,6 +205,45 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
         vreg[i] = t < seq_len ? load8(p + 4 * i * 8 * EB) : make_uint4(0, 0, 0, 0);
     }
   };
+  // ---- bf16: direct copies.  Wave w copies block w of tile kt (16 keys, the
+  // tile's keys 16w .. 16w+15) of K and V; instruction j writes LDS chunks
+  // 64j .. 64j+63 of the block, lane i chunk 64j + i, fetching the global
+  // chunk that the swizzle puts there.
+  auto block_id = [&](int kt) -> int32_t {                  // wave-uniform
+    return kt * kBN + kBlock * w < seq_len ? bt_row[kt * 4 + w] : -1;
+  };
+  auto dma = [&](int kt, int32_t bid, int buf) {
+    (void)kt;
+    if (bid < 0) return;                                    // block past the context
+    const int64_t base = ((int64_t)bid * blk_stride + head_off) * EB;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const int P = 64 * j + lane;
+      const int key = P / CH;                               // key in the block
+      const int c = (P % CH) ^ ((kBlock * w + key) & (CH - 1));
+      const int64_t off = base + (int64_t)(key * D + c * 8) * EB;
+      const int slot = kBlock * CH * w + 64 * j;
+      // (destinations as plain LDS offsets: the copies' completion is
+      // awaited explicitly before the barrier that publishes the buffer,
+      // and the compiler then adds no wait before reads of the other one)
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void_t*)(uintptr_t)lds_offset(&sm.k[buf][slot]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void_t*)(uintptr_t)lds_offset(&sm.vt[buf][slot]),
+                                       16, 0, 0);
+    }
+  };
+  // once this wave's copies have landed: zero the V rows of its block past
+  // the context (unwritten slots may hold NaN, and P = 0 times NaN is NaN;
+  // K rows there are masked by select)
+  auto zero_tail = [&](int kt, int buf) {
+    const int t0 = kt * kBN + kBlock * w;
+    if (t0 + kBlock <= seq_len) return;                     // wave-uniform
+    uint4* vl = &sm.vt[buf][kBlock * CH * w];
+    for (int idx = lane; idx < kBlock * CH; idx += 64)
+      if (t0 + idx / CH >= seq_len) vl[idx] = make_uint4(0, 0, 0, 0);
+  };
+  auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
   auto stage = [&](int buf) {
     uint4* kl = &sm.k[buf][0];
     uint16_t* vt16 = reinterpret_cast<uint16_t*>(&sm.vt[buf][0]);
@@ -210,14 +268,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[b][v] = 0.f;
 
-  fetch(0);
-  stage(0);
+  int32_t bid_next = -1;
+  if constexpr (FP8) {
+    fetch(0);
+    stage(0);
+  } else {
+    dma(0, block_id(0), 0);
+    if (n_tiles > 1) bid_next = block_id(1);
+    wait_copies();
+    zero_tail(0, 0);
+  }
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < n_tiles;
-    if (more) fetch(kt + 1);
+    if (more) {
+      if constexpr (FP8) {
+        fetch(kt + 1);
+      } else {
+        dma(kt + 1, bid_next, buf ^ 1);
+        if (kt + 2 < n_tiles) bid_next = block_id(kt + 2);
+      }
+    }
     const int k0 = kt * kBN;
     if (k0 <= wave_pmax) {                      // some key of the tile is visible to the wave
       // -- S^T = K Q^T for the two 32-key halves of the tile
@@ -287,18 +360,53 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
                                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         }
       // -- O^T += V^T P^T
+      if constexpr (FP8) {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d = 32 * db + lq;
+        for (int db = 0; db < DBLK; ++db) {
+          const int d = 32 * db + lq;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int chunk = (2 * ks + lh) ^ ((d >> 1) & 7);
-          const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
-          oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+          for (int ks = 0; ks < 4; ++ks) {
+            const int chunk = (2 * ks + lh) ^ ((d >> 1) & 7);
+            const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
+            oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+          }
+        }
+      } else {
+        // V^T fragment (d = 32db + lane % 32, keys 32b + 16s' + 4lh + 8(t/4)
+        // + t%4 for element t: the order of P^T's k-step (b, s')) from
+        // row-major V by two transposing reads.  Lane gi of 16-lane group G
+        // addresses row 32b + 16s' + 4lh + gi/4 (+8 for the second read),
+        // elements 32db + 16(G&1) + 4(gi%4) .. +3; the transpose hands lane
+        // gi of the group those rows' element 32db + 16(G&1) + gi.
+        const int G = lane / 16, gi = lane % 16;
+        const char* vbuf = reinterpret_cast<const char*>(&sm.vt[buf][0]);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int r0 = 32 * (ks / 2) + 16 * (ks % 2) + 4 * lh + gi / 4;
+            const int e0 = 32 * db + 16 * (G & 1) + 4 * (gi % 4);
+            uint2 part[2];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+              const int r = r0 + 8 * hp;
+              const int slot = r * CH + ((e0 / 8) ^ (r & (CH - 1)));
+              part[hp] = lds_read_tr16(vbuf + 16 * slot + 2 * (e0 % 8));
+            }
+            const uint4 vf = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+            oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+          }
         }
       }
     }
-    if (more) stage(buf ^ 1);
+    if (more) {
+      if constexpr (FP8) {
+        stage(buf ^ 1);
+      } else {
+        wait_copies();
+        zero_tail(kt + 1, buf ^ 1);
+      }
+    }
     __syncthreads();
   }
 
