@@ -146,6 +146,26 @@ __device__ __forceinline__ Words<N> load_words(const uint8_t* p) {
   return r;
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
+// (required by the untyped buffer loads), no swizzle, no index stride.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// N words at byte offset `off` of a buffer resource (out-of-range lanes read 0)
+template <int N, int AUX>
+__device__ __forceinline__ Words<N> rsrc_words(__amdgpu_buffer_rsrc_t r, int off) {
+  Words<N> w;
+  if constexpr (N == 4) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    w.w[0] = v.x; w.w[1] = v.y; w.w[2] = v.z; w.w[3] = v.w;
+  } else if constexpr (N == 2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+    w.w[0] = v.x; w.w[1] = v.y;
+  } else {
+    w.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+  }
+  return w;
+}
+
 constexpr int kBtChunk = 1024;   // block-table entries staged in LDS at a time
 
 // ---------------------------------------------------------------------------
@@ -239,6 +259,39 @@ struct WaveDecoder {
       t.v[i] = load_words<VW, kStream>(vt + ((vrg + 4 * i) * D + vcol) * EB);
   }
 
+  // The same tile through buffer resources spanning just this tile: with
+  // live == false the resources have zero length, so every lane's load
+  // returns 0 without touching memory (a prefetch past the wave's last
+  // block costs no traffic, and the load stays unconditional, which keeps
+  // the compiler's wait counts exact).
+  __device__ __forceinline__ void load_tile_rsrc(Tile& t, const uint8_t* kbase,
+                                                 const uint8_t* vbase, int32_t phys, int g,
+                                                 int num_kv_heads, bool live) const {
+    constexpr int kTileBytes = kBlock * D * EB;
+    constexpr int kAux = kStream ? 2 : 0;           // cache policy: nt (streaming)
+    // the tile address and length are wave-uniform by construction; made
+    // scalar here so the resources live in SGPRs whatever the caller's
+    // control flow lets the compiler prove
+    const int64_t off0 = tile_offset(phys, g, num_kv_heads, D) * EB;
+    const int64_t off =
+        (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off0 >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)off0));
+    const int nrec = __builtin_amdgcn_readfirstlane(live ? kTileBytes : 0);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < RK; ++i)
+#pragma unroll
+      for (int k = 0; k < KCH; ++k)
+        t.k[i][k] = rsrc_words<KW, kAux>(kr, (krow0 + (64 / LPR) * i) * (D * EB) +
+                                                 (kc + LPR * k) * KCHB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      t.v[i] = rsrc_words<VW, kAux>(vr, ((vrg + 4 * i) * D + vcol) * EB);
+  }
+
   // Fold one block (tokens tok0 .. tok0+15, those >= t_end excluded) into
   // the state.  `slab` is this wave's [16][GCP] float LDS buffer.
   __device__ __forceinline__ void compute(const Tile& t, int tok0, int t_end, float* slab) {
@@ -302,8 +355,8 @@ struct WaveDecoder {
       // max over all rows of head kc: lanes with equal kc
       if constexpr (LPR == 4) bm = fmaxf(bm, dpp<kRowRor4>(bm));
       bm = fmaxf(bm, dpp<kRowRor8>(bm));
-      bm = fmaxf(bm, xor_lanes(bm, 16));
-      bm = fmaxf(bm, xor_lanes(bm, 32));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
       const float m_new = fmaxf(m_run, bm);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -430,10 +483,10 @@ struct WaveDecoder {
     }
     l += dpp<kRowRor8>(l);
     mt = fmaxf(mt, dpp<kRowRor8>(mt));
-    l += xor_lanes(l, 16);
-    mt = fmaxf(mt, xor_lanes(mt, 16));
-    l += xor_lanes(l, 32);
-    mt = fmaxf(mt, xor_lanes(mt, 32));
+    l = sum_xor16(l);
+    mt = max_xor16(mt);
+    l = sum_xor32(l);
+    mt = max_xor32(mt);
     l_part = l;
     m_true = mt;
 #pragma unroll
@@ -441,16 +494,17 @@ struct WaveDecoder {
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
         float v = acc[j][e];
-        v += xor_lanes(v, 16);
-        v += xor_lanes(v, 32);
+        v = sum_xor16(v);
+        v = sum_xor32(v);
         acc[j][e] = v;
       }
   }
 };
 
 // Stream n blocks through the decoder with PD tiles in flight.  phys_of(it)
-// must accept it >= n (clamped by the caller) so the prefetch is
-// unconditional and the compiler's wait counts stay exact.
+// must accept it >= n (clamped by the caller): the prefetch is issued
+// unconditionally, so the compiler's wait counts stay exact, and a prefetch
+// past the last block is a zero-length buffer load that moves no data.
 template <int PD, class Dec, class PhysFn, class TokFn>
 __device__ __forceinline__ void stream_blocks(Dec& dec, int n, const uint8_t* kbase,
                                               const uint8_t* vbase, int g, int num_kv_heads,
@@ -459,32 +513,32 @@ __device__ __forceinline__ void stream_blocks(Dec& dec, int n, const uint8_t* kb
   using Tile = typename Dec::Tile;
   if constexpr (PD == 1) {
     Tile ta, tb;
-    dec.load_tile(ta, kbase, vbase, phys_of(0), g, num_kv_heads);
+    dec.load_tile_rsrc(ta, kbase, vbase, phys_of(0), g, num_kv_heads, true);
     int32_t pn = phys_of(1);
     for (int it = 0; it < n; it += 2) {
-      dec.load_tile(tb, kbase, vbase, pn, g, num_kv_heads);
+      dec.load_tile_rsrc(tb, kbase, vbase, pn, g, num_kv_heads, it + 1 < n);
       pn = phys_of(it + 2);
       dec.compute(ta, tok0_of(it), t_end, slab0);
       if (it + 1 >= n) break;
-      dec.load_tile(ta, kbase, vbase, pn, g, num_kv_heads);
+      dec.load_tile_rsrc(ta, kbase, vbase, pn, g, num_kv_heads, it + 2 < n);
       pn = phys_of(it + 3);
       dec.compute(tb, tok0_of(it + 1), t_end, slab1);
     }
   } else {                                  // two tiles in flight while computing
     Tile t0, t1, t2;
-    dec.load_tile(t0, kbase, vbase, phys_of(0), g, num_kv_heads);
-    dec.load_tile(t1, kbase, vbase, phys_of(1), g, num_kv_heads);
+    dec.load_tile_rsrc(t0, kbase, vbase, phys_of(0), g, num_kv_heads, true);
+    dec.load_tile_rsrc(t1, kbase, vbase, phys_of(1), g, num_kv_heads, 1 < n);
     int32_t pn = phys_of(2);
     for (int it = 0; it < n; it += 3) {
-      dec.load_tile(t2, kbase, vbase, pn, g, num_kv_heads);
+      dec.load_tile_rsrc(t2, kbase, vbase, pn, g, num_kv_heads, it + 2 < n);
       pn = phys_of(it + 3);
       dec.compute(t0, tok0_of(it), t_end, (it & 1) ? slab1 : slab0);
       if (it + 1 >= n) break;
-      dec.load_tile(t0, kbase, vbase, pn, g, num_kv_heads);
+      dec.load_tile_rsrc(t0, kbase, vbase, pn, g, num_kv_heads, it + 3 < n);
       pn = phys_of(it + 4);
       dec.compute(t1, tok0_of(it + 1), t_end, (it & 1) ? slab0 : slab1);
       if (it + 2 >= n) break;
-      dec.load_tile(t1, kbase, vbase, pn, g, num_kv_heads);
+      dec.load_tile_rsrc(t1, kbase, vbase, pn, g, num_kv_heads, it + 4 < n);
       pn = phys_of(it + 5);
       dec.compute(t2, tok0_of(it + 2), t_end, (it & 1) ? slab1 : slab0);
     }
@@ -558,7 +612,9 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
   }
 
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
+  // wave index, scalar: the compiler then knows every per-wave count and
+  // loop bound below is wave-uniform (no exec-masked loop control)
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
 
   if (t_end <= t_begin) {                         // empty context: zero row
@@ -719,10 +775,13 @@ __global__ __launch_bounds__(kBalWaves * 64) void decode_balanced_kernel(
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= R; i += blockDim.x) prefix_out[i] = C[i];
 
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);     // scalar wave index
   const int G = a.num_q_heads / a.num_kv_heads;
   const int U = a.num_kv_heads * n_chunks;                  // units per request
-  const int64_t N = (int64_t)C[R] * U;
+  // (LDS reads are per lane to the compiler: the wave-uniform values below
+  // are made scalar, so the loop bounds and tile addresses stay uniform)
+  const int64_t N = (int64_t)__builtin_amdgcn_readfirstlane(C[R]) * U;
   const int64_t W = (int64_t)gridDim.x * kBalWaves;
   const int64_t k = (int64_t)blockIdx.x * kBalWaves + w;
   const int64_t x_end = bal_bound(k + 1, N, W);
@@ -747,9 +806,10 @@ __global__ __launch_bounds__(kBalWaves * 64) void decode_balanced_kernel(
       const int mid = (lo + hi + 1) >> 1;
       if ((int64_t)C[mid] * U <= x) lo = mid; else hi = mid - 1;
     }
-    const int r = lo;
-    const int nb = C[r + 1] - C[r];
-    const int64_t local = x - (int64_t)C[r] * U;
+    const int r = __builtin_amdgcn_readfirstlane(lo);
+    const int cr = __builtin_amdgcn_readfirstlane(C[r]);
+    const int nb = __builtin_amdgcn_readfirstlane(C[r + 1]) - cr;
+    const int64_t local = x - (int64_t)cr * U;
     const int j = (int)(local / nb);
     const int b0 = (int)(local - (int64_t)j * nb);
     const int b1 = (int)min<int64_t>(nb, b0 + (x_end - x));

@@ -148,8 +148,8 @@ struct MfmaDecoder {
       for (int u = 0; u < 4; ++u)
         amax = fmaxf(amax, fmaxf(fabsf(bf16lo(raw[s][u])), fabsf(bf16hi(raw[s][u]))));
     }
-    amax = fmaxf(amax, xor_lanes(amax, 16));
-    amax = fmaxf(amax, xor_lanes(amax, 32));      // max |q| of head col
+    amax = max_xor16(amax);
+    amax = max_xor32(amax);      // max |q| of head col
     // exponent e with amax * 2^e in [2^14, 2^15); 0 for an all-zero head
     int e = 0;
     if (amax > 0.f && amax < INFINITY) e = 14 - (int)((__float_as_uint(amax) >> 23) & 0xff) + 127;
@@ -199,8 +199,8 @@ struct MfmaDecoder {
       x[i] = (full || tok < t_end) ? xv : -INFINITY;
       bm = fmaxf(bm, x[i]);
     }
-    bm = fmaxf(bm, xor_lanes(bm, 16));
-    bm = fmaxf(bm, xor_lanes(bm, 32));            // max over the head's 16 tokens
+    bm = max_xor16(bm);
+    bm = max_xor32(bm);            // max over the head's 16 tokens
     m_true = fmaxf(m_true, bm);
     const bool grow = bm > m_run + kMTau;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform and rare: move the max
@@ -255,8 +255,8 @@ struct MfmaDecoder {
 
   // l over the four lane groups (every lane of a head then holds it)
   __device__ __forceinline__ void finish() {
-    l_part += xor_lanes(l_part, 16);
-    l_part += xor_lanes(l_part, 32);
+    l_part = sum_xor16(l_part);
+    l_part = sum_xor32(l_part);
   }
 };
 
@@ -359,8 +359,8 @@ struct MfmaDecoderB {
       x[i] = (full || tok < t_end) ? xv : -INFINITY;
       bm = fmaxf(bm, x[i]);
     }
-    bm = fmaxf(bm, xor_lanes(bm, 16));
-    bm = fmaxf(bm, xor_lanes(bm, 32));
+    bm = max_xor16(bm);
+    bm = max_xor32(bm);
     m_true = fmaxf(m_true, bm);
     const bool grow = bm > m_run + kMTau;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -411,8 +411,8 @@ struct MfmaDecoderB {
   }
 
   __device__ __forceinline__ void finish() {
-    l_part += xor_lanes(l_part, 16);
-    l_part += xor_lanes(l_part, 32);
+    l_part = sum_xor16(l_part);
+    l_part = sum_xor32(l_part);
   }
 };
 

@@ -136,6 +136,48 @@ constexpr int kRowRor8 = 0x128;   // rotate right by 8 within 16 lanes (== xor 8
 
 __device__ __forceinline__ float xor_lanes(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+// All-reduce of x with lane (l ^ 32) or (l ^ 16) on the vector ALU.
+// v_permlane32_swap a, b exchanges lanes 32-63 of a with lanes 0-31 of b, so
+// afterwards a = [a lanes 0-31, b lanes 0-31] and b = [a lanes 32-63,
+// b lanes 32-63] (v_permlane16_swap the same with 16-lane rows: a = rows
+// a0 b0 a2 b2, b = a1 b1 a3 b3; checked on gfx950).  With a = b = x every
+// lane ends with x of both partners in {a, b}, in a lane-dependent order --
+// hence only commutative reductions here.  No LDS crossbar traffic, unlike
+// ds_bpermute.  Written as asm with both registers read-write: through the
+// compiler builtin, ROCm 7.2's backend reads the first result in place of
+// the second when both inputs carry the same value.  The s_nop gives the
+// two wait states a VALU write needs before a permlane reads it.
+template <bool ROW16>
+__device__ __forceinline__ void swap_halves(float x, float& r0, float& r1) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  if constexpr (ROW16)
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  r0 = __builtin_bit_cast(float, a);
+  r1 = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float r0, r1;
+  swap_halves<false>(x, r0, r1);
+  return r0 + r1;
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float r0, r1;
+  swap_halves<false>(x, r0, r1);
+  return fmaxf(r0, r1);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float r0, r1;
+  swap_halves<true>(x, r0, r1);
+  return r0 + r1;
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float r0, r1;
+  swap_halves<true>(x, r0, r1);
+  return fmaxf(r0, r1);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;

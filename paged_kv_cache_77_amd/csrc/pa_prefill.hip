@@ -332,7 +332,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[b][v]);
-      tmax = fmaxf(tmax, xor_lanes(tmax, 32)) * sc;
+      tmax = max_xor32(tmax) * sc;
       // -- lazy rescale: move the max only when it grows by more than 2^8.
       // Key 0 is visible to every query, so m_run is finite after tile 0.
       if (tmax > m_run + 8.0f) {
@@ -411,7 +411,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   }
 
   // ---- finalize: l over both lane halves, O = A / l, write bf16 rows
-  const float l_tot = l_run + xor_lanes(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   if (q_ok && wave_on) {
     float inv = 1.f / l_tot;
     if constexpr (FP8) inv *= *a.v_scale;

@@ -126,6 +126,39 @@ def test_decode_wide_batch_both_wave_counts(ctx_hi, cache):
     check_bf16(dv.bits_of(out), oracle.decode(w), "pa_decode")
 
 
+@pytest.mark.parametrize("R,hq,hkv,d,ctx_hi,alibi", [
+    (128, 32, 8, 128, 600, False),     # 1024 work-groups, 4 waves each
+    (75, 16, 8, 64, 3000, False),      # odd count, G = 2
+    (64, 24, 8, 128, 2500, True),      # G = 3 with ALiBi, 8 waves each
+    (40, 32, 8, 128, 16384, False),    # 320 work-groups, long contexts
+])
+def test_decode_wide_ranked_batches(R, hq, hkv, d, ctx_hi, alibi):
+    """More (request, KV head) work-groups than compute units, launched
+    longest first (each work-group ranks the seq_lens on the device).  Ties,
+    contexts 1/16/17, and rows whose seq_len is set to 0 on the device (their
+    output must be zero, and they rank last) are included."""
+    _announce(f"decode wide ranked R={R} hq={hq} hkv={hkv} d={d} ctx<={ctx_hi} alibi={alibi}")
+    rng = np.random.default_rng(R * 7 + hq)
+    ctx = [int(x) for x in rng.integers(1, ctx_hi + 1, size=R)]
+    ctx[0] = ctx[1] = ctx_hi                       # tie at the top
+    ctx[2:5] = [1, 16, 17]
+    ctx[5] = ctx[6]                                # tie in the middle
+    w = wl.make_workload(name="t", seq_lens=ctx, q_lens=[1] * R, num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, seed=90 + R, writes_new_kv=False,
+                         bt_extra_cols=2, alibi=alibi)
+    dd = dv.to_device(w)
+    empty = [7, R - 1]
+    dd.seq_lens[empty] = 0
+    ref = oracle.decode(w)
+    out = _out(w)
+    dv.run_decode(dd, out)
+    torch.cuda.synchronize()
+    bits = dv.bits_of(out)
+    keep = [r for r in range(R) if r not in empty]
+    check_bf16(bits[keep], ref[keep], "ranked single pass")
+    assert np.all(bits[empty] == 0)
+
+
 def test_decode_empty_context_is_zero():
     _announce("decode seq_len 0")
     w = wl.make_workload(name="t", seq_lens=[0, 20], q_lens=[0, 0], num_q_heads=4,
