@@ -50,7 +50,8 @@ DESCR = {
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_device.h", "pa_prefill.hip",
+    for f in ("pa_decode.hip", "pa_decode_wave.h", "pa_decode_mfma.hip", "pa_device.h",
+              "pa_prefill.hip",
               "pa_cache_ops.hip", "pa_launch.h"):
         p = os.path.join(ROOT, "paged_kv_cache_77_amd", "csrc", f)
         if os.path.exists(p):

@@ -280,8 +280,11 @@ int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t
  * alibi_slopes[h] * (t - p) (P1 §3.2.4's decode term, whose query sits at
  * p = seq_len - 1).  Requests with q_len <= 1 take the decode
  * path (P1 §5.2 split_decodes_and_prefills, threshold 1); q_len == 0 writes
- * nothing.  The K/V of this step's tokens must already be in the cache
- * (pa_reshape_and_cache first).
+ * nothing.  With bf16 caches, GQA groups below 8 and at least a device's
+ * worth of decode work-groups, both kinds of rows run in one launch (the
+ * prefill tiles and the decode rows share the compute units); otherwise the
+ * decode rows, then the prefill rows.  The K/V of this step's tokens must
+ * already be in the cache (pa_reshape_and_cache first).
  *  out, q : bf16 [num_tokens][num_q_heads][head_dim]
  *  max_query_len, max_seq_len : host upper bounds (grid sizing only)
  */

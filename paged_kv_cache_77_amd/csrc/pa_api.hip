@@ -365,8 +365,6 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
                                  k_scale, v_scale, alibi_slopes);
   a.out = out;
   a.query_start_loc = query_start_loc;
-  PA_TRY(hip_status(pa::launch_decode(a, false, st)));
-  if (max_query_len <= 1) return PA_OK;
   pa::PrefillArgs p;
   memset(&p, 0, sizeof(p));
   p.q = q;
@@ -389,6 +387,11 @@ int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int3
   p.max_query_len = max_query_len;
   p.max_seq_len = max_seq_len;
   p.scale = scale;
+  // both kinds of rows in one launch where that applies, else the decode
+  // rows and then the prefill rows
+  if (pa::varlen_fused_applies(p)) return hip_status(pa::launch_varlen(p, a, st));
+  PA_TRY(hip_status(pa::launch_decode(a, false, st)));
+  if (max_query_len <= 1) return PA_OK;
   return hip_status(pa::launch_prefill(p, st));
 }
 

@@ -103,4 +103,12 @@ struct PrefillArgs {
 // Rows of requests with q_len > 1 (the decode kernel takes the others).
 hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream);
 
+// Both kinds of rows of a varlen batch in one launch (prefill tiles and
+// decode rows side by side on every compute unit); varlen_fused_applies
+// says whether launch_varlen handles the batch (bf16 caches, GQA groups
+// below 8, enough decode rows to fill the device).
+bool varlen_fused_applies(const PrefillArgs& args);
+hipError_t launch_varlen(const PrefillArgs& prefill, const DecodeArgs& decode,
+                         hipStream_t stream);
+
 }  // namespace pa

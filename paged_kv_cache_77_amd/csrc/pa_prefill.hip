@@ -30,8 +30,11 @@
 // (ds_read_b64_tr_b16).  FP8 caches are converted to bf16 in registers on
 // the way: K is stored as above, V transposed (d-major) with the key
 // permutation and a swizzle on d >> 1.  All tiles are double-buffered.
+// P^T enters the PV products as a bf16 high part plus a bf16 remainder (two
+// MFMAs per V^T fragment), so the probabilities keep ~16 significant bits.
 #include <algorithm>
 
+#include "pa_decode_wave.h"
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -60,6 +63,24 @@ constexpr int kBN = 64;         // keys per tile
 constexpr int kWaves = 4;
 constexpr int kQW = 32;         // queries per wave
 constexpr int kMaxPrefillGroups = 4096;   // work-groups of one launch (a multiple of 8)
+// Prefill and decode rows of a varlen batch in one launch where it applies
+// (0: always the two launches, decode rows then prefill rows).
+#ifndef PA_VARLEN_FUSED
+#define PA_VARLEN_FUSED 1
+#endif
+// Tiles in flight per decode wave in the fused launch (its work-groups have
+// 256 VGPRs per wave, the prefill role's budget).
+#ifndef PA_VARLEN_DECODE_PREFETCH
+#define PA_VARLEN_DECODE_PREFETCH 1
+#endif
+// Prefill items placed before the decode units in the fused launch, in
+// multiples of the compute-unit count (measured on the mixed batch of 128
+// decode rows and a 2048-token chunk: 2 -- every item first, decode units
+// filling the slots the items free -- 0.775 ms; 1: 0.80; 0: 0.80; two
+// launches: 0.82).
+#ifndef PA_VARLEN_FIRST
+#define PA_VARLEN_FIRST 2
+#endif
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -344,8 +365,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[b][v] *= alpha;
       }
-      // -- P^T as bf16 B operands: k-step (b, s') takes accumulator rows 8s'..8s'+7
-      uint4 pf[4];
+      // -- P^T as bf16 B operands: k-step (b, s') takes accumulator rows
+      // 8s'..8s'+7.  Each probability is split into a bf16 high part (pf) and
+      // the bf16 of the remainder (pl), both multiplied into O^T, so the
+      // weights keep ~16 significant bits: one bf16 rounding (2^-9 relative)
+      // times |v| of a few units would otherwise take a peaked softmax's
+      // output near the 1e-2 bound.
+      uint4 pf[4], pl[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -356,8 +382,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
             p[e] = fast_exp2(fmaf(s[b][8 * sp + e], sc, -m_run));   // -inf -> 0
             l_run += p[e];
           }
-          pf[2 * b + sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+            lw[e] = pack_bf16x2(p[2 * e] - bf16lo(hw[e]), p[2 * e + 1] - bf16hi(hw[e]));
+          }
+          pf[2 * b + sp] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          pl[2 * b + sp] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
       // -- O^T += V^T P^T
       if constexpr (FP8) {
@@ -369,6 +401,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
             const int chunk = (2 * ks + lh) ^ ((d >> 1) & 7);
             const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
             oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+            oacc[db] = mfma32(vf, pl[ks], oacc[db]);
           }
         }
       } else {
@@ -395,6 +428,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
             }
             const uint4 vf = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
             oacc[db] = mfma32(vf, pf[ks], oacc[db]);
+            oacc[db] = mfma32(vf, pl[ks], oacc[db]);
           }
         }
       }
@@ -439,25 +473,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 // the tile count (decode rows cost no work-groups).
 // With direct != 0 (few requests) the grid is (tiles * U, num_reqs) instead:
 // one item per work-group, request blockIdx.y, no search.
+// Work items k = first, first + stride, ... (k < num_items) of one
+// work-group; with snake, its j-th item is j * stride + first for even j and
+// (j + 1) * stride - 1 - first for odd j (persistent workers then pair the
+// long query tiles of a causal chunk with the short ones).
 template <int D, bool FP8, bool ALIBI>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
-                                                                 int64_t num_items,
-                                                                 int direct) {
-  __shared__ PrefillSmem<D> sm;
-  __shared__ int sched[2];
+__device__ __forceinline__ void prefill_items(const PrefillArgs& a, PrefillSmem<D>& sm,
+                                              int* sched, int64_t first, int64_t stride,
+                                              int64_t num_items, bool snake) {
   int hpw, qbw, nhc;
   prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
   const int U = a.num_kv_heads * nhc;
   const int QT = kQW * qbw;
-  if (direct) {
-    const int r = blockIdx.y, tile = blockIdx.x / U;
-    const int q_len = a.query_start_loc[r + 1] - a.query_start_loc[r];
-    if (q_len <= 1 || tile * QT >= q_len) return;
-    prefill_item<D, FP8, ALIBI>(a, sm, r, tile, blockIdx.x % U);
-    return;
-  }
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
-  for (int64_t k = blockIdx.x; k < num_items; k += gridDim.x) {
+  for (int64_t j = 0;; ++j) {
+    const int64_t k = (snake && (j & 1)) ? (j + 1) * stride - 1 - first : j * stride + first;
+    if (k >= num_items) break;
     const int64_t kt = k / U;
     if (w == 0) {
       int64_t base = 0;
@@ -495,10 +526,97 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
     const int r = __builtin_amdgcn_readfirstlane(sched[0]);
     const int tile = __builtin_amdgcn_readfirstlane(sched[1]);
     __syncthreads();
-    if (r < 0) break;                                        // past the last tile
+    if (r < 0) break;            // past the last tile (later items are larger still)
     prefill_item<D, FP8, ALIBI>(a, sm, r, tile, (int)(k % U));
     __syncthreads();
   }
+}
+
+// The work items are the query tiles of the requests with q_len > 1, in
+// request order, times the KV-head groups: item k is flattened tile k / U of
+// KV-head group k % U (U = num_kv_heads * nhc).  Wave 0 of a work-group finds
+// the request holding a flattened tile by a running prefix over the
+// requests' tile counts, 64 requests per step.  Work-groups take items
+// blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized by a bound on
+// the tile count (decode rows cost no work-groups).
+// With direct != 0 (few requests) the grid is (tiles * U, num_reqs) instead:
+// one item per work-group, request blockIdx.y, no search.
+template <int D, bool FP8, bool ALIBI>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
+                                                                 int64_t num_items,
+                                                                 int direct) {
+  __shared__ PrefillSmem<D> sm;
+  __shared__ int sched[2];
+  if (direct) {
+    int hpw, qbw, nhc;
+    prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
+    const int U = a.num_kv_heads * nhc;
+    const int QT = kQW * qbw;
+    const int r = blockIdx.y, tile = blockIdx.x / U;
+    const int q_len = a.query_start_loc[r + 1] - a.query_start_loc[r];
+    if (q_len <= 1 || tile * QT >= q_len) return;
+    prefill_item<D, FP8, ALIBI>(a, sm, r, tile, blockIdx.x % U);
+    return;
+  }
+  prefill_items<D, FP8, ALIBI>(a, sm, sched, blockIdx.x, gridDim.x, num_items, false);
+}
+
+// Prefill tiles and decode rows of one varlen batch in one launch (bf16
+// caches, vector-ALU decode).  The grid is three runs of work-groups, handed
+// out in order: n_first prefill items (one each), then the n_dec (decode
+// row, KV head x head chunk) units, then the remaining prefill items.  Free
+// slots of the compute units are refilled from the next run as work-groups
+// finish, so the MFMA/LDS-bound prefill and the HBM-bound decode share the
+// compute units instead of running one after the other.
+template <int D, bool ALIBI, int GC>
+__global__ __launch_bounds__(kWaves * 64, 2) void varlen_kernel(PrefillArgs p, DecodeArgs a,
+                                                                int64_t num_items, int n_first,
+                                                                int n_dec, int n_chunks) {
+  __shared__ union {
+    PrefillSmem<D> pf;
+    DecodeSmem<D, GC, false, kWaves> dc;
+  } sm;
+  __shared__ int sched[2];
+  const int b = blockIdx.x;
+  if (b < n_first || b >= n_first + n_dec) {
+    const int64_t item = b < n_first ? b : (int64_t)b - n_dec;
+    prefill_items<D, false, ALIBI>(p, sm.pf, sched, item, num_items, num_items, false);
+    return;
+  }
+  const int u = b - n_first;
+  const int U = a.num_kv_heads * n_chunks;
+  decode_unit<D, GC, false, kWaves, false, PA_VARLEN_DECODE_PREFETCH>(a, sm.dc, u / U, u % U, 0,
+                                                                      n_chunks);
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Prefill items of a launch: an upper bound on the query tiles of the
+// requests with q_len > 1, times the KV-head groups.  Tiles <= sum over the
+// prefill requests of (q_len / QT + 1) <= T / QT + #prefill requests, with
+// #prefill requests <= min(num_reqs, T / 2) and each tile count <=
+// ceil(max_query_len / QT).
+static int64_t prefill_item_bound(const PrefillArgs& a) {
+  int hpw, qbw, nhc;
+  prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
+  const int QT = kQW * qbw;
+  const int64_t T = a.num_tokens;
+  const int64_t per_req = (a.max_query_len + QT - 1) / QT;
+  const int64_t nreq_bound = std::min<int64_t>(a.num_reqs, T / 2);
+  const int64_t tiles = std::min<int64_t>((T + QT - 1) / QT + nreq_bound, per_req * nreq_bound);
+  return tiles * a.num_kv_heads * nhc;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
@@ -506,14 +624,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   int hpw, qbw, nhc;
   prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
   const int QT = kQW * qbw;
-  // tiles <= sum over prefill requests of (q_len / QT + 1) <= T / QT + #prefill
-  // requests, with #prefill requests <= min(num_reqs, T / 2) and each tile
-  // count <= ceil(max_query_len / QT)
-  const int64_t T = a.num_tokens;
   const int64_t per_req = (a.max_query_len + QT - 1) / QT;
-  const int64_t nreq_bound = std::min<int64_t>(a.num_reqs, T / 2);
-  const int64_t tiles = std::min<int64_t>((T + QT - 1) / QT + nreq_bound, per_req * nreq_bound);
-  const int64_t num_items = tiles * a.num_kv_heads * nhc;
+  const int64_t num_items = prefill_item_bound(a);
   if (num_items == 0) return hipSuccess;
   // few requests: the direct grid wastes at most a few work-groups
   const int direct = a.num_reqs <= 4 ? 1 : 0;
@@ -539,6 +651,51 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   }
 #undef PA_PREFILL
   return hipGetLastError();
+}
+
+bool varlen_fused_applies(const PrefillArgs& p) {
+  if (!PA_VARLEN_FUSED || p.cache_dtype != 0 || p.max_query_len <= 1 || p.num_reqs < 2)
+    return false;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  if (G >= 8) return false;                     // decode rows on the matrix cores
+  const int cus = cu_count();
+  // at least one round of decode work-groups besides the prefill rows
+  return cus > 0 && (int64_t)(p.num_reqs - 1) * p.num_kv_heads >= cus;
+}
+
+template <int D, int GC>
+static hipError_t launch_varlen_t(const PrefillArgs& p, const DecodeArgs& a, hipStream_t st) {
+  const int64_t num_items = prefill_item_bound(p);
+  const int n_first = (int)std::min<int64_t>(num_items, (int64_t)PA_VARLEN_FIRST * cu_count());
+  const int n_chunks = 1;                       // GC == G here (G < 8)
+  const int n_dec = a.num_reqs * a.num_kv_heads * n_chunks;
+  const int64_t groups = num_items + n_dec;
+  if (p.alibi_slopes)
+    hipLaunchKernelGGL((varlen_kernel<D, true, GC>), dim3((unsigned)groups), dim3(kWaves * 64), 0,
+                       st, p, a, num_items, n_first, n_dec, n_chunks);
+  else
+    hipLaunchKernelGGL((varlen_kernel<D, false, GC>), dim3((unsigned)groups), dim3(kWaves * 64), 0,
+                       st, p, a, num_items, n_first, n_dec, n_chunks);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_varlen_d(const PrefillArgs& p, const DecodeArgs& a, hipStream_t st) {
+  switch (p.num_q_heads / p.num_kv_heads) {
+    case 1: return launch_varlen_t<D, 1>(p, a, st);
+    case 2: return launch_varlen_t<D, 2>(p, a, st);
+    case 3: return launch_varlen_t<D, 3>(p, a, st);
+    case 4: return launch_varlen_t<D, 4>(p, a, st);
+    case 5: return launch_varlen_t<D, 5>(p, a, st);
+    case 6: return launch_varlen_t<D, 6>(p, a, st);
+    default: return launch_varlen_t<D, 7>(p, a, st);
+  }
+}
+
+hipError_t launch_varlen(const PrefillArgs& p, const DecodeArgs& a, hipStream_t st) {
+  DecodeArgs b = a;
+  b.lpt = 0;
+  return p.head_dim == 64 ? launch_varlen_d<64>(p, b, st) : launch_varlen_d<128>(p, b, st);
 }
 
 }  // namespace pa

@@ -110,6 +110,30 @@ def test_chunked_equals_whole():
     check_bf16(halves, ref, "two chunks")
 
 
+@pytest.mark.parametrize("hq,hkv,d,prefill_first,alibi", [
+    (32, 8, 128, False, False), (32, 8, 128, True, True), (16, 8, 64, False, False),
+    (8, 8, 128, True, False)])
+def test_varlen_one_launch_batches(hq, hkv, d, prefill_first, alibi):
+    """Batches with enough decode rows ((rows - 1) x KV heads >= the compute
+    units) that pa_prefill_varlen runs prefill tiles and decode rows in one
+    launch; every row is checked against the oracle.  Includes a whole
+    prompt, a chunk on a cached prefix, a row with no queries, contexts 1, 16
+    and 17, and both row orders."""
+    _announce(f"varlen one launch hq={hq} hkv={hkv} d={d} prefill_first={prefill_first} "
+              f"alibi={alibi}")
+    rng = np.random.default_rng(hq * 10 + d)
+    n_dec = 40
+    dec = [int(x) for x in rng.integers(1, 1500, size=n_dec)]
+    dec[:3] = [1, 16, 17]
+    pre_sl, pre_ql = [500, 129, 50], [300, 129, 0]
+    sl = pre_sl + dec if prefill_first else dec + pre_sl
+    ql = pre_ql + [1] * n_dec if prefill_first else [1] * n_dec + pre_ql
+    w = wl.make_workload(name="t", seq_lens=sl, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, seed=70 + hq + d, bt_extra_cols=2, alibi=alibi)
+    got, kp, vp = _run(w)
+    check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "varlen one launch")
+
+
 def test_config4_full_size_sampled():
     """Full mixed batch (128 decode rows + 2048-token chunk on 6144 cached
     tokens) in the benchmark's launch configuration; the oracle computes a
