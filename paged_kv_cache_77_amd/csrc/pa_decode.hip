@@ -31,10 +31,19 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
   // With a.lpt, blockIdx.z is a rank: the request with the rank-th longest
   // context (ties by index), so the hardware hands out the longest units
   // first and the short ones fill the tail (longest-processing-time order).
+  // With a.lpt_half, the grid is at most two work-groups per compute unit:
+  // requests z < lpt_half (one work-group per compute unit) take ranks z,
+  // the rest ranks R - 1 - (z - lpt_half), so the work-group that joins a
+  // compute unit later takes a short unit beside a long one.
   int r = blockIdx.z;
   if constexpr (!PART) {
     if (a.lpt) {
       const int R = a.num_reqs;
+      // with a.lpt_half > 0 the requests from a.lpt_half on take the
+      // remaining ranks backwards, so the second round's work-groups pair
+      // the shortest units with the longest
+      const int z = blockIdx.z, hf = a.lpt_half;
+      const int target = (hf > 0 && z >= hf) ? R - 1 - (z - hf) : z;
       for (int i = threadIdx.x; i < R; i += WAVES * kWave) sm.bt[i] = a.seq_lens[i];
       __syncthreads();
       for (int j = threadIdx.x; j < R; j += WAVES * kWave) {
@@ -44,7 +53,7 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
           const int lk = sm.bt[k];
           rank += (lk > lj || (lk == lj && k < j)) ? 1 : 0;
         }
-        if (rank == (int)blockIdx.z) sm.sched = j;
+        if (rank == target) sm.sched = j;
       }
       __syncthreads();
       r = __builtin_amdgcn_readfirstlane(sm.sched);
@@ -375,6 +384,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 // ---------------------------------------------------------------------------
 // dispatch
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <int D, int GC, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStream_t st) {
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -397,7 +420,17 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     b.lpt = (PA_DECODE_LPT && a.query_start_loc == nullptr && a.num_reqs <= kLptMaxReqs) ? 1 : 0;
     const int64_t min_len = groups < 384 ? PA_DECODE_WAVES_SINGLE_MIN_LEN
                                          : 2 * PA_DECODE_WAVES_SINGLE_MIN_LEN;
-    if (groups < 768 && a.max_seq_len >= min_len) {
+    const int cus = device_cu_count();
+    if (b.lpt && cus > 0 && groups > cus && groups <= 2 * cus) {
+      // one to two rounds: 4-wave work-groups, all resident at once (two per
+      // compute unit), ranks paired long with short (measured on MI355X:
+      // 64 requests x 8 KV heads, contexts U[512, 4096]: 0.111 vs 0.114 ms
+      // with 8 waves in two rounds; 64 x 2048 tokens: 0.090 vs 0.096 ms)
+      b.lpt_half = std::max(1, cus / (int)grid.y);
+      constexpr int WAVES = PA_DECODE_WAVES_SPLIT;
+      hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,
+                         st, b, n_chunks);
+    } else if (groups < 768 && a.max_seq_len >= min_len) {
       constexpr int WAVES = PA_DECODE_WAVES_SINGLE;
       hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, false, PD>), grid, dim3(WAVES * 64), 0,
                          st, b, n_chunks);

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t max_num_partitions;
   int32_t part_begin, part_end;     // partitioned mode: partitions written (end 0 = all)
   int32_t lpt;                      // set by the launcher: longest requests first
+  int32_t lpt_half;                 // set by the launcher: > 0 pairs ranks (see decode_kernel)
   float scale;
 };
 
