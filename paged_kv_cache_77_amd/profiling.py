@@ -51,7 +51,7 @@ RUNS = {
                  "of 2176 tokens, then pa_prefill_varlen (decode kernel for the decode rows, "
                  "MFMA prefill kernel for the chunk)",
         "args": "--config 4",
-        "keys": {"config4_varlen": ["pa::decode_kernel", "pa::prefill_kernel"],
+        "keys": {"config4_varlen": ["pa::varlen_kernel"],
                  "config4_prefill": ["pa::prefill_kernel"]},
     },
     "shared_prefix_fp8": {
