@@ -81,6 +81,21 @@ def decode_bytes(w) -> dict:
             "unique_total": kv_unique + qo + bt + 4 * w.num_reqs}
 
 
+def shared_prefix_blocks(w, partition_size: int) -> int:
+    """Leading block-table entries every request shares with request 0 (what
+    a prefix cache knows), in whole partitions: request 0 must hold them all
+    and every other request uses the same physical blocks for them."""
+    import numpy as np
+    n0 = (int(w.seq_lens[0]) + 15) // 16
+    common = n0
+    for r in range(1, w.num_reqs):
+        n = min(n0, (int(w.seq_lens[r]) + 15) // 16)
+        neq = np.nonzero(w.block_table[r, :n] != w.block_table[0, :n])[0]
+        common = min(common, int(neq[0]) if neq.size else (n0 if n == n0 else common))
+    per = partition_size // 16
+    return common // per * per
+
+
 def decode_kernel_name(w) -> str:
     """The kernel the library's decode dispatch runs for this shape: the
     matrix-core kernel for FP8 caches with GQA groups of 4+ and bf16 caches
@@ -146,14 +161,15 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     d = dv.to_device(w, "cuda")
     nbytes = decode_bytes(w)
     if path == "auto":
-        path = "split" if cfg == 3 else "single"
-    P = partition_size or (w.partition_size if cfg == 3 else 1024)
+        path = {3: "split", 5: "shared"}.get(cfg, "single")
+    P = partition_size or (w.partition_size if cfg in (3, 5) else 1024)
+    shared = shared_prefix_blocks(w, P) if path == "shared" else 0
     is_prefill = cfg == 4
     T = w.num_tokens
     sm = torch.empty((max(T, 1),), dtype=torch.int64, device="cuda")
     rows = T if is_prefill else w.num_reqs
     out = torch.empty((rows, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-    bufs = dv.partial_buffers(d, P) if (path == "split" and not is_prefill) else None
+    bufs = dv.partial_buffers(d, P) if (path in ("split", "shared") and not is_prefill) else None
     ws = dv.decode_workspace(d) if path == "balanced" else None
     stream = torch.cuda.current_stream()
     ev = []
@@ -166,6 +182,8 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
             dv.run_decode(d, out)
         elif path == "balanced":
             dv.run_decode_balanced(d, out, ws)
+        elif path == "shared":
+            dv.run_decode_shared_prefix(d, out, shared, P, bufs)
         else:
             tmp, ml, es = bufs
             pa.pa_decode_partitioned(d.layout, d.q, d.k_cache, d.v_cache, d.block_table,
@@ -234,7 +252,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
         return round(v[min(len(v) - 1, int(q * len(v)))], 5)
     r = {"cfg": cfg, "w": w, "nbytes": nbytes, "ms_step": ms_step, "kern_ms": kern_ms,
          "path": "varlen" if is_prefill else path,
-         "partition_size": P if (path == "split" and not is_prefill) else None,
+         "partition_size": P if (path in ("split", "shared") and not is_prefill) else None,
          "kernel_ms_stats": {
              "train": {"mean": round(kern_ms, 5), "reps": reps,
                        "how": "events around back-to-back calls on the launch stream"},
@@ -282,6 +300,12 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     elif path == "balanced":
         r["kernel"] = "decode_balanced_kernel + balanced_merge_kernel"
         r["kbytes"] = nbytes["total"]
+    elif path == "shared":
+        r["kernel"] = (f"pa_decode_shared_prefix: shared_prefix_kernel (MFMA, {shared} shared "
+                       f"blocks) + {decode_kernel_name(w)} (tails, split-KV P={P}) + "
+                       "merge_kernel")
+        r["kbytes"] = nbytes["total"]
+        r["shared_blocks"] = shared
     else:
         r["kernel"] = f"{decode_kernel_name(w)} (single pass)"
         r["kbytes"] = nbytes["total"]
@@ -299,7 +323,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
         G = w.num_q_heads // w.num_kv_heads
         flops = 4 * G * w.head_dim * nbytes["tokens"] * w.num_kv_heads
         tf = flops / (kern_ms * 1e-3) / 1e12
-        if decode_kernel_name(w) == "decode_mfma_kernel":
+        if decode_kernel_name(w) == "decode_mfma_kernel" or path == "shared":
             r["alu"] = {"bound": "mfma", "kernel": r["kernel"], "achieved": round(tf, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -387,9 +411,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", choices=["auto", "split", "single", "balanced"], default="auto",
-                    help="decode path; auto = split-KV for the long-context workload, "
-                         "single pass otherwise (measured faster for these batches)")
+    ap.add_argument("--path", choices=["auto", "split", "single", "balanced", "shared"],
+                    default="auto",
+                    help="decode path; auto = split-KV for the long-context workload, the "
+                         "shared-prefix decode for the shared-prefix workload, single pass "
+                         "otherwise (measured faster for these batches)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition size in tokens (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -460,6 +486,10 @@ def main() -> int:
             o = measure(cfg, "auto", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
             other[f"config{cfg}"] = summary(o)
             del o
+        # the shared-prefix workload through the per-request decode (pa_decode)
+        o = measure(5, "single", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
+        other["config5_per_request_decode"] = summary(o)
+        del o
         other["block_manager"] = block_manager_rate()
         res["other_workloads"] = other
     print(json.dumps(res))

@@ -222,6 +222,43 @@ int pa_decode_partitioned_range(const pa_kv_layout* layout, const void* q, int32
                                 float* exp_sums, void* stream);
 
 /*
+ * Decode for a batch whose requests begin with the same cached blocks
+ * (prefix caching: every request maps its first logical blocks onto the
+ * same physical blocks, P1 §4.1 and the shared-block figure of P4 §4).  The
+ * result is pa_decode's.  The shared prefix is read once per KV head: its
+ * key partitions are multiplied into the decode queries of all requests
+ * together on the matrix cores (K.Q^T and V^T.P^T over 64-key tiles, each
+ * partition's (m, l, O) written as the split-KV partials of P1 §3.2.7);
+ * the private tails go through the split-KV decode (partitions from
+ * shared_blocks * 16 / partition_size on); pa_merge_partitions' merge
+ * (P1 §3.2.9) combines the two.
+ *  shared_blocks : leading block-table entries the requests share: request
+ *                  0 holds the whole prefix (seq_lens[0] >= 16 *
+ *                  shared_blocks) and every other request's entries among
+ *                  the first shared_blocks that it uses equal request 0's
+ *                  (the caller knows this from its prefix cache; the
+ *                  kernels read the prefix through request 0's row).
+ *                  shared_blocks * 16 must be a multiple of partition_size
+ *                  and <= max_seq_len; other requests may be shorter than
+ *                  the prefix.
+ *  partition_size: tokens per partition, a multiple of 64
+ *  tmp_out, max_logits, exp_sums : caller-owned scratch laid out as for
+ *                  pa_decode_partitioned (max_num_partitions >=
+ *                  ceil(max_seq_len / partition_size)); overwritten.
+ *  out           : bf16 [num_reqs][num_q_heads][head_dim]
+ * Other arguments as pa_decode.  Three launches on `stream` (prefix
+ * partials, tail partials, merge); calls sharing scratch race.
+ */
+int pa_decode_shared_prefix(const pa_kv_layout* layout, void* out, const void* q,
+                            int32_t num_reqs, int32_t num_q_heads, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                            const float* k_scale, const float* v_scale,
+                            const float* alibi_slopes, int32_t shared_blocks,
+                            int32_t partition_size, int32_t max_num_partitions, float* tmp_out,
+                            float* max_logits, float* exp_sums, void* stream);
+
+/*
  * Split-KV decode, merge stage (P1 §3.2.9 equations):
  *     m = max_j m_j,  L = sum_j l_j e^(m_j - m),
  *     out = sum_j tmp_out_j * l_j e^(m_j - m) / L     -> bf16, round to nearest even

@@ -268,6 +268,76 @@ int pa_decode_partitioned_range(const pa_kv_layout* layout, const void* q, int32
   return hip_status(pa::launch_decode(a, true, (hipStream_t)stream));
 }
 
+int pa_decode_shared_prefix(const pa_kv_layout* layout, void* out, const void* q,
+                            int32_t num_reqs, int32_t num_q_heads, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                            const float* k_scale, const float* v_scale,
+                            const float* alibi_slopes, int32_t shared_blocks,
+                            int32_t partition_size, int32_t max_num_partitions, float* tmp_out,
+                            float* max_logits, float* exp_sums, void* stream) {
+  PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                       bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
+  if (partition_size <= 0 || partition_size % 64 != 0 || shared_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  const int64_t shared_tokens = (int64_t)shared_blocks * layout->block_size;
+  if (shared_tokens % partition_size != 0 || shared_tokens > max_seq_len)
+    return PA_ERR_INVALID_ARG;
+  const int64_t need = ((int64_t)max_seq_len + partition_size - 1) / partition_size;
+  if (max_num_partitions < 1 || max_num_partitions < need) return PA_ERR_INVALID_ARG;
+  if (num_reqs == 0) return PA_OK;
+  if (!out || !aligned16(out) || !tmp_out || !max_logits || !exp_sums || !aligned16(tmp_out))
+    return PA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (shared_tokens > 0) {
+    pa::PrefillArgs p;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.seq_lens = seq_lens;
+    p.block_table = block_table;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.alibi_slopes = alibi_slopes;
+    p.num_reqs = num_reqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = layout->num_kv_heads;
+    p.head_dim = layout->head_dim;
+    p.cache_dtype = layout->cache_dtype;
+    p.bt_stride = bt_stride;
+    p.max_seq_len = max_seq_len;
+    p.scale = scale;
+    p.tmp_out = tmp_out;
+    p.max_logits = max_logits;
+    p.exp_sums = exp_sums;
+    p.partition_size = partition_size;
+    p.max_num_partitions = max_num_partitions;
+    p.shared_tokens = (int32_t)shared_tokens;
+    PA_TRY(hip_status(pa::launch_shared_prefix(p, st)));
+  }
+  // the private tails: one open-ended record per request (partition
+  // first_tail, tokens shared_tokens .. seq_len), merged with the prefix's
+  const int32_t first_tail = (int32_t)(shared_tokens / partition_size);
+  if (first_tail < need) {
+    pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
+                                   block_table, bt_stride, seq_lens, max_seq_len, scale,
+                                   k_scale, v_scale, alibi_slopes);
+    a.tmp_out = tmp_out;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    a.part_begin = first_tail;
+    a.part_end = first_tail + 1;
+    a.open_last = 1;
+    PA_TRY(hip_status(pa::launch_decode(a, true, st)));
+  }
+  return hip_status(pa::launch_merge(out, tmp_out, max_logits, exp_sums, seq_lens, num_reqs,
+                                     num_q_heads, layout->head_dim, partition_size,
+                                     max_num_partitions, st, first_tail + 1));
+}
+
 int pa_merge_partitions(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

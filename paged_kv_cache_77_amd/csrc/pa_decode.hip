@@ -313,14 +313,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ tmp_out,
     const float* __restrict__ max_logits, const float* __restrict__ exp_sums,
     const int32_t* __restrict__ seq_lens, int32_t num_q_heads, int32_t partition_size,
-    int32_t max_num_partitions) {
+    int32_t max_num_partitions, int32_t max_used) {
   constexpr int TPR = D / 4;                    // threads per partition row
   constexpr int PG = kMergeThreads / TPR;       // partition rows per step
   __shared__ float wgt[kMergeMaxParts];
   __shared__ float red[kMergeThreads];
   __shared__ f32x4_t part[PG][TPR];
   const int r = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-  const int n = (seq_lens[r] + partition_size - 1) / partition_size;
+  int n = (seq_lens[r] + partition_size - 1) / partition_size;
+  if (max_used > 0) n = min(n, max_used);      // the last record may be an open tail
   const int64_t base = ((int64_t)r * num_q_heads + h) * max_num_partitions;
   const int pg = tid / TPR, c = tid % TPR;
 
@@ -531,17 +532,17 @@ int balanced_max_reqs() { return kBalMaxReqs; }
 hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
-                        int32_t max_num_partitions, hipStream_t st) {
+                        int32_t max_num_partitions, hipStream_t st, int32_t max_used) {
   if (num_reqs == 0) return hipSuccess;
   dim3 grid(num_q_heads, num_reqs);
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, st, (uint16_t*)out, tmp_out,
                        max_logits, exp_sums, seq_lens, num_q_heads, partition_size,
-                       max_num_partitions);
+                       max_num_partitions, max_used);
   else
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, st, (uint16_t*)out, tmp_out,
                        max_logits, exp_sums, seq_lens, num_q_heads, partition_size,
-                       max_num_partitions);
+                       max_num_partitions, max_used);
   return hipGetLastError();
 }
 

@@ -488,7 +488,8 @@ __global__ __launch_bounds__(kMWaves * 64, FP8 ? (ALIBI ? 3 : PA_MFMA_MINW_FP8) 
   if constexpr (PART) {
     t_begin = part * a.partition_size;
     if (t_begin >= seq_len) return;
-    t_end = min(seq_len, t_begin + a.partition_size);
+    t_end = (a.open_last && part == a.part_end - 1) ? seq_len
+                                                    : min(seq_len, t_begin + a.partition_size);
   }
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);

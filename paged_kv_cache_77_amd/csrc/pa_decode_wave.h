@@ -589,7 +589,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, DecodeSmem<D, G
   if constexpr (PART) {
     t_begin = part * a.partition_size;
     if (t_begin >= seq_len) return;
-    t_end = min(seq_len, t_begin + a.partition_size);
+    t_end = (a.open_last && part == a.part_end - 1) ? seq_len
+                                                    : min(seq_len, t_begin + a.partition_size);
   }
 
   const int tid = threadIdx.x;

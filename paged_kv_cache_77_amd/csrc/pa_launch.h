@@ -27,6 +27,7 @@ struct DecodeArgs {
   int32_t partition_size;           // tokens per partition (partitioned mode)
   int32_t max_num_partitions;
   int32_t part_begin, part_end;     // partitioned mode: partitions written (end 0 = all)
+  int32_t open_last;                // partition part_end - 1 runs to seq_len (a tail record)
   int32_t lpt;                      // set by the launcher: longest requests first
   int32_t lpt_half;                 // set by the launcher: > 0 pairs ranks (see decode_kernel)
   float scale;
@@ -78,10 +79,12 @@ hipError_t launch_decode_balanced(const DecodeArgs& args, void* workspace, hipSt
 int64_t balanced_workspace_bytes(int num_reqs, int num_q_heads, int num_kv_heads, int head_dim);
 int balanced_max_reqs();
 
+// max_used > 0: at most that many partitions per request are merged (the
+// last one may be an open-ended tail record); 0: ceil(seq_len / P).
 hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits,
                         const float* exp_sums, const int32_t* seq_lens, int32_t num_reqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
-                        int32_t max_num_partitions, hipStream_t stream);
+                        int32_t max_num_partitions, hipStream_t stream, int32_t max_used = 0);
 
 struct PrefillArgs {
   const void* q;
@@ -99,6 +102,13 @@ struct PrefillArgs {
   int32_t num_tokens;               // query rows in the batch
   int32_t max_query_len, max_seq_len;
   float scale;
+  // shared-prefix decode (launch_shared_prefix): partials of the prefix's
+  // partitions, as the split-KV decode writes them
+  float* tmp_out;
+  float* max_logits;
+  float* exp_sums;
+  int32_t partition_size, max_num_partitions;
+  int32_t shared_tokens;            // prefix length (a multiple of partition_size)
 };
 
 // Rows of requests with q_len > 1 (the decode kernel takes the others).
@@ -109,6 +119,11 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream);
 // says whether launch_varlen handles the batch (bf16 caches, GQA groups
 // below 8, enough decode rows to fill the device).
 bool varlen_fused_applies(const PrefillArgs& args);
+
+// The shared prefix's partitions of a shared-prefix decode: every request's
+// decode query against the key partitions [0, shared_tokens / P) of request
+// 0's table, on the matrix cores, written as split-KV partials.
+hipError_t launch_shared_prefix(const PrefillArgs& args, hipStream_t stream);
 hipError_t launch_varlen(const PrefillArgs& prefill, const DecodeArgs& decode,
                          hipStream_t stream);
 

@@ -28,8 +28,7 @@
 // registers), both row-major with a 16-byte-chunk XOR swizzle; the V^T
 // fragments of the PV products come from gfx950's transposing LDS read
 // (ds_read_b64_tr_b16).  FP8 caches are converted to bf16 in registers on
-// the way: K is stored as above, V transposed (d-major) with the key
-// permutation and a swizzle on d >> 1.  All tiles are double-buffered.
+// the way and stored in the same layout.  All tiles are double-buffered.
 // P^T enters the PV products as a bf16 high part plus a bf16 remainder (two
 // MFMAs per V^T fragment), so the probabilities keep ~16 significant bits.
 #include <algorithm>
@@ -87,16 +86,10 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Slot of key k (0..63) inside the V^T rows: within each group of 16 keys,
-// bits 2 and 3 are swapped (the order the S^T accumulators hold keys in).
-__device__ __forceinline__ int vt_slot(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 template <int D>
 struct PrefillSmem {
   uint4 k[2][kBN * D / 8];        // [key][16-byte chunk ^ (key & 15)]
-  uint4 vt[2][D * kBN / 8];       // [d][16-byte chunk of slots ^ ((d >> 1) & 7)]
+  uint4 vt[2][kBN * D / 8];       // V, the same layout (read transposed)
 };
 
 // Work-group shape: hpw heads x qbw 32-query blocks (hpw * qbw == kWaves).
@@ -108,7 +101,14 @@ __host__ __device__ inline void prefill_shape(int G, int& hpw, int& qbw, int& nh
 
 // One work item: query tile `tile` (kQW * qbw queries) of request r, KV head
 // group `unit` (KV head unit / nhc, head chunk unit % nhc).
-template <int D, bool FP8, bool ALIBI>
+// SHARED (the prefix part of pa_decode_shared_prefix): the decode queries of
+// every request, flattened per KV head (query j = (request j / G, head
+// g * G + j % G)), against key partition `r` of the prefix the requests
+// share (request 0's table), tile `tile` = 128 flattened queries, `unit` = KV
+// head; the result is that partition's (m, l, O) partials.  A query sits at
+// position seq_len - 1 of its request, so the causal mask below is its
+// context bound.
+template <int D, bool FP8, bool ALIBI, bool SHARED = false>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D>& sm, int r,
                                              int tile, int unit) {
   constexpr int CH = D / 8;               // 16-byte chunks per bf16 row
@@ -121,39 +121,70 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   const int G = Hq / Hkv;
   int hpw, qbw, nhc;
   prefill_shape(G, hpw, qbw, nhc);
-  const int g = unit / nhc, hc = unit - g * nhc;
-  const int qlo = a.query_start_loc[r];
-  const int q_len = a.query_start_loc[r + 1] - qlo;
-  const int i0 = tile * kQW * qbw;                          // first query of the tile
-  const int seq_len = a.seq_lens[r];
-  const int pos0 = seq_len - q_len;                         // position of query 0
-
   // the wave index is uniform: keep it (and all per-wave values) scalar
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lq = lane % 32, lh = lane / 32;
-  const int hw = w % hpw, qbl = w / hpw;                    // head and query block of the wave
-  const bool wave_on = (qbl < qbw) && (hc * kWaves + hw < G);
-  const int h = g * G + hc * kWaves + (wave_on ? hw : 0);
-  const int wq0 = i0 + qbl * kQW;                           // first query of the wave
+
+  int g, seq_len, kt_begin, n_tiles, p_q, wave_pmin, wave_pmax, h;
+  bool q_ok, wave_on;
+  int64_t q_row;                           // query row of this lane (token index)
+  const int32_t* bt_row;
+  if constexpr (SHARED) {
+    g = unit;
+    const int nq = a.num_reqs * G;                          // flattened queries of the head
+    const int j = (tile * kWaves + w) * kQW + lq;
+    q_ok = j < nq;
+    const int rq = q_ok ? j / G : 0;
+    h = g * G + (q_ok ? j - rq * G : 0);
+    q_row = rq;
+    seq_len = a.shared_tokens;                              // keys of the prefix
+    kt_begin = r * (a.partition_size / kBN);
+    n_tiles = min((r + 1) * a.partition_size, seq_len) / kBN;
+    p_q = q_ok ? a.seq_lens[rq] - 1 : -1;                   // context bound of the query
+    int pmin = q_ok ? p_q : INT32_MAX, pmax = p_q;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      pmin = min(pmin, __shfl_xor(pmin, m, 64));
+      pmax = max(pmax, __shfl_xor(pmax, m, 64));
+    }
+    wave_pmin = __builtin_amdgcn_readfirstlane(pmin);
+    wave_pmax = __builtin_amdgcn_readfirstlane(pmax);
+    wave_on = true;
+    bt_row = a.block_table;                                 // the shared rows: request 0's
+  } else {
+    const int hc = unit - (unit / nhc) * nhc;
+    g = unit / nhc;
+    const int qlo = a.query_start_loc[r];
+    const int q_len = a.query_start_loc[r + 1] - qlo;
+    const int i0 = tile * kQW * qbw;                        // first query of the tile
+    seq_len = a.seq_lens[r];
+    const int pos0 = seq_len - q_len;                       // position of query 0
+    const int hw = w % hpw, qbl = w / hpw;                  // head and query block of the wave
+    wave_on = (qbl < qbw) && (hc * kWaves + hw < G);
+    h = g * G + hc * kWaves + (wave_on ? hw : 0);
+    const int wq0 = i0 + qbl * kQW;                         // first query of the wave
+    const int qi = wq0 + lq;                                // query index in request
+    q_ok = qi < q_len;
+    q_row = qlo + (q_ok ? qi : 0);
+    p_q = pos0 + qi;                                        // this lane's query position
+    wave_pmin = pos0 + wq0;                                 // first query position of the wave
+    wave_pmax = wave_on ? pos0 + min(wq0 + kQW, q_len) - 1 : -1;   // -1: no work
+    const int kend = pos0 + min(i0 + kQW * qbw, q_len);     // keys the work-group needs
+    kt_begin = 0;
+    n_tiles = (kend + kBN - 1) / kBN;
+    bt_row = a.block_table + (int64_t)r * a.bt_stride;
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T): query lq, d = 16k + 8lh .. +8
-  const int qi = wq0 + lq;                                  // query index in request
-  const bool q_ok = qi < q_len;
   uint4 qf[KSTEPS];
   {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(qlo + (q_ok ? qi : 0)) * Hq + h) * D;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (q_row * Hq + h) * D;
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) {
       const uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * k + 8 * lh);
       qf[k] = q_ok ? v : make_uint4(0, 0, 0, 0);
     }
   }
-  const int p_q = pos0 + qi;                                // this lane's query position
-  const int wave_pmin = pos0 + wq0;                         // first query position of the wave
-  const int wave_pmax = wave_on ? pos0 + min(wq0 + kQW, q_len) - 1 : -1;   // -1: no work
-  const int kend = pos0 + min(i0 + kQW * qbw, q_len);       // keys the work-group needs
-  const int n_tiles = (kend + kBN - 1) / kBN;
 
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
@@ -162,16 +193,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   const float slope = ALIBI ? a.alibi_slopes[h] * kLog2e : 0.f;
   const float sc = ALIBI ? 1.f : qk_scale;
 
-  const int32_t* bt_row = a.block_table + (int64_t)r * a.bt_stride;
   constexpr int EB = FP8 ? 1 : 2;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
 
-  // ---- global -> registers -> LDS staging of one 64-key tile (4 blocks).
-  // K: thread chunk i is (key tid/CH + (256/CH) i, 8 elements at tid % CH), so
-  // rows stream contiguously.  V: key tid % 64 (lane-fast), chunk tid/64 + 4i,
-  // so each transposed 2-byte LDS store of a wave covers consecutive slots.
-  // All LDS offsets are loop-invariant and computed once.
+  // ---- FP8: global -> registers -> LDS staging of one 64-key tile (4
+  // blocks).  Thread chunk i of K and of V is (key tid/CH + (256/CH) i, 8
+  // elements at tid % CH), so rows stream contiguously; the LDS offsets are
+  // loop-invariant and computed once.
   constexpr int NCH = kBN * CH / (kWaves * 64);             // chunks per thread per tensor
   const int kc_chunk = tid % CH;
   int k_key[NCH], k_lds[NCH];
@@ -180,33 +209,25 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
     k_key[i] = tid / CH + (kWaves * 64 / CH) * i;
     k_lds[i] = k_key[i] * CH + (kc_chunk ^ (k_key[i] & (CH - 1)));
   }
-  const int v_key = tid % kBN;
-  const int v_slot = vt_slot(v_key);
-  int v_lds[8];                                             // u16 offsets for e = 0..7, chunk 0
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {     // row d = 8c + e; c has the parity of v_c0
-    const int dsw = ((4 * ((tid / kBN) & 1)) + (e >> 1)) & 7;          // (d >> 1) & 7
-    v_lds[e] = 64 * e + (((v_slot >> 3) ^ dsw) << 3) + (v_slot & 7);
-  }
-  const int v_c0 = tid / kBN;                               // chunk of i = 0; + 4 per i
-
-  uint4 kreg[NCH], vreg[NCH];
-  auto load8 = [&](const uint8_t* p) -> uint4 {             // 8 elements -> 8 bf16
-    if constexpr (FP8) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(p);
-      const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
-      return make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                        pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
-    } else {
-      return *reinterpret_cast<const uint4*>(p);
-    }
+  // the raw codes stay in registers while the current tile is computed and
+  // are converted to bf16 only when staged (converting at load time would
+  // make the loop wait for the next tile's loads before computing)
+  uint2 kraw[NCH], vraw[NCH];
+  bool live[NCH];                                           // key of chunk i < seq_len
+  auto cvt8 = [](uint2 raw) -> uint4 {                      // 8 codes -> 8 bf16
+    const f32x4_t lo = fp8x4_to_f32(raw.x), hi = fp8x4_to_f32(raw.y);
+    return make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                      pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
   };
   const int64_t head_off = (int64_t)g * (kBlock * D);
   const int64_t blk_stride = (int64_t)Hkv * (kBlock * D);
-  auto fetch = [&](int kt) {
-    // block ids of the tile's 4 blocks (entries past the context are not read)
+  // block ids of tile kt's 4 blocks in lanes 0..3 (entries past the context
+  // are not read); loaded one tile ahead of the data they address
+  auto tile_bids = [&](int kt) -> int32_t {
     const int jb_lane = lane & 3;
-    const int32_t bid_vec = (kt * kBN + jb_lane * kBlock < seq_len) ? bt_row[kt * 4 + jb_lane] : 0;
+    return (kt < n_tiles && kt * kBN + jb_lane * kBlock < seq_len) ? bt_row[kt * 4 + jb_lane] : 0;
+  };
+  auto fetch = [&](int kt, int32_t bid_vec) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int t = kt * kBN + k_key[i];
@@ -214,16 +235,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
       const int32_t bid = __builtin_amdgcn_readlane(bid_vec, jb);
       const uint8_t* p = kbase + (bid * blk_stride + head_off +
                                   (int64_t)((k_key[i] % kBlock) * D + kc_chunk * 8)) * EB;
-      kreg[i] = t < seq_len ? load8(p) : make_uint4(0, 0, 0, 0);
-    }
-    {
-      const int t = kt * kBN + v_key;
-      const int32_t bid = __shfl(bid_vec, v_key / kBlock, kWave);
-      const uint8_t* p = vbase + (bid * blk_stride + head_off +
-                                  (int64_t)((v_key % kBlock) * D + v_c0 * 8)) * EB;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i)                         // past the context: zero
-        vreg[i] = t < seq_len ? load8(p + 4 * i * 8 * EB) : make_uint4(0, 0, 0, 0);
+      // (unconditional: a key past the context has block id 0, a valid
+      // block; its codes are replaced by zeros when staged)
+      live[i] = t < seq_len;
+      kraw[i] = *reinterpret_cast<const uint2*>(p);
+      vraw[i] = *reinterpret_cast<const uint2*>(vbase + (p - kbase));
     }
   };
   // ---- bf16: direct copies.  Wave w copies block w of tile kt (16 keys, the
@@ -265,24 +281,23 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
+  // FP8: K and V rows, converted to bf16, in the same swizzled row-major
+  // layout the bf16 copies produce (V^T fragments then come from the
+  // transposing LDS reads, as for bf16 caches)
   auto stage = [&](int buf) {
     uint4* kl = &sm.k[buf][0];
-    uint16_t* vt16 = reinterpret_cast<uint16_t*>(&sm.vt[buf][0]);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) kl[k_lds[i]] = kreg[i];
+    uint4* vl = &sm.vt[buf][0];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      uint16_t* vrow = vt16 + 512 * (v_c0 + 4 * i);
-      const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vrow[v_lds[e]] = (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
+      kl[k_lds[i]] = live[i] ? cvt8(kraw[i]) : make_uint4(0, 0, 0, 0);
+      vl[k_lds[i]] = live[i] ? cvt8(vraw[i]) : make_uint4(0, 0, 0, 0);
     }
   };
 
   // ---- running state of this lane's query (keys split between lane halves);
   // m_run is in scaled log2 units, scores s are raw dot products (times sc).
   float m_run = -INFINITY, l_run = 0.f;
+  float m_true = -INFINITY;                 // exact max (partials of SHARED)
   f32x16_t oacc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
@@ -291,22 +306,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 
   int32_t bid_next = -1;
   if constexpr (FP8) {
-    fetch(0);
+    fetch(kt_begin, tile_bids(kt_begin));
+    bid_next = tile_bids(kt_begin + 1);
     stage(0);
   } else {
-    dma(0, block_id(0), 0);
-    if (n_tiles > 1) bid_next = block_id(1);
+    dma(kt_begin, block_id(kt_begin), 0);
+    if (kt_begin + 1 < n_tiles) bid_next = block_id(kt_begin + 1);
     wait_copies();
-    zero_tail(0, 0);
+    zero_tail(kt_begin, 0);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt_begin; kt < n_tiles; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < n_tiles;
     if (more) {
       if constexpr (FP8) {
-        fetch(kt + 1);
+        fetch(kt + 1, bid_next);
+        bid_next = tile_bids(kt + 2);
       } else {
         dma(kt + 1, bid_next, buf ^ 1);
         if (kt + 2 < n_tiles) bid_next = block_id(kt + 2);
@@ -354,6 +371,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[b][v]);
       tmax = max_xor32(tmax) * sc;
+      if constexpr (SHARED) m_true = fmaxf(m_true, tmax);
       // -- lazy rescale: move the max only when it grows by more than 2^8.
       // Key 0 is visible to every query, so m_run is finite after tile 0.
       if (tmax > m_run + 8.0f) {
@@ -392,19 +410,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
           pl[2 * b + sp] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
       // -- O^T += V^T P^T
-      if constexpr (FP8) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int d = 32 * db + lq;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int chunk = (2 * ks + lh) ^ ((d >> 1) & 7);
-            const uint4 vf = sm.vt[buf][d * (kBN / 8) + chunk];
-            oacc[db] = mfma32(vf, pf[ks], oacc[db]);
-            oacc[db] = mfma32(vf, pl[ks], oacc[db]);
-          }
-        }
-      } else {
+      {
         // V^T fragment (d = 32db + lane % 32, keys 32b + 16s' + 4lh + 8(t/4)
         // + t%4 for element t: the order of P^T's k-step (b, s')) from
         // row-major V by two transposing reads.  Lane gi of 16-lane group G
@@ -444,12 +450,39 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
     __syncthreads();
   }
 
-  // ---- finalize: l over both lane halves, O = A / l, write bf16 rows
+  // ---- finalize: l over both lane halves, O = A / l, write bf16 rows (or
+  // the partition's partials: max logit in natural-log units, exp-sum
+  // relative to it, O normalised -- the split-KV record of P1 §3.2.7)
   const float l_tot = sum_xor32(l_run);
+  if constexpr (SHARED) {
+    if (q_ok) {
+      const bool any = l_tot > 0.f;          // false: no key of the partition is visible
+      float inv = any ? 1.f / l_tot : 0.f;
+      if constexpr (FP8) inv *= *a.v_scale;
+      const int64_t idx = (q_row * Hq + h) * a.max_num_partitions + r;
+      float* op = a.tmp_out + idx * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * db + 8 * i + 4 * lh;
+          // (select, not a product: with no key the accumulators hold NaN)
+          *reinterpret_cast<f32x4_t*>(op + d) =
+              any ? f32x4_t{oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv,
+                            oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv}
+                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      if (lh == 0) {
+        a.max_logits[idx] = any ? m_true * kLn2 : -INFINITY;
+        a.exp_sums[idx] = any ? l_tot * fast_exp2(m_run - m_true) : 0.f;
+      }
+    }
+    return;
+  }
   if (q_ok && wave_on) {
     float inv = 1.f / l_tot;
     if constexpr (FP8) inv *= *a.v_scale;
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(qlo + qi) * Hq + h) * D;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (q_row * Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -561,6 +594,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
   prefill_items<D, FP8, ALIBI>(a, sm, sched, blockIdx.x, gridDim.x, num_items, false);
 }
 
+// Shared-prefix partials: work-group (query block of 128 flattened decode
+// queries, key partition, KV head).
+template <int D, bool FP8, bool ALIBI>
+__global__ __launch_bounds__(kWaves * 64, 2) void shared_prefix_kernel(PrefillArgs a) {
+  __shared__ PrefillSmem<D> sm;
+  prefill_item<D, FP8, ALIBI, true>(a, sm, blockIdx.y, blockIdx.x, blockIdx.z);
+}
+
 // Prefill tiles and decode rows of one varlen batch in one launch (bf16
 // caches, vector-ALU decode).  The grid is three runs of work-groups, handed
 // out in order: n_first prefill items (one each), then the n_dec (decode
@@ -650,6 +691,33 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     }
   }
 #undef PA_PREFILL
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_prefix(const PrefillArgs& a, hipStream_t st) {
+  if (a.num_reqs == 0 || a.shared_tokens <= 0) return hipSuccess;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int64_t nq = (int64_t)a.num_reqs * G;
+  const dim3 grid((unsigned)((nq + kWaves * kQW - 1) / (kWaves * kQW)),
+                  (unsigned)(a.shared_tokens / a.partition_size), (unsigned)a.num_kv_heads);
+  const bool fp8 = a.cache_dtype != 0;
+  const bool alibi = a.alibi_slopes != nullptr;
+#define PA_SHARED(DV, F8, AL) \
+  hipLaunchKernelGGL((shared_prefix_kernel<DV, F8, AL>), grid, dim3(kWaves * 64), 0, st, a)
+  if (a.head_dim == 64) {
+    if (fp8) {
+      if (alibi) PA_SHARED(64, true, true); else PA_SHARED(64, true, false);
+    } else {
+      if (alibi) PA_SHARED(64, false, true); else PA_SHARED(64, false, false);
+    }
+  } else {
+    if (fp8) {
+      if (alibi) PA_SHARED(128, true, true); else PA_SHARED(128, true, false);
+    } else {
+      if (alibi) PA_SHARED(128, false, true); else PA_SHARED(128, false, false);
+    }
+  }
+#undef PA_SHARED
   return hipGetLastError();
 }
 

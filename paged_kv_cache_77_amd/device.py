@@ -10,7 +10,8 @@ import numpy as np
 import torch
 
 from . import (PA_CACHE_BF16, PA_CACHE_FP8_E4M3, make_layout, pa_compute_slot_mapping,
-               pa_decode, pa_decode_partitioned, pa_merge_partitions, pa_prefill_varlen,
+               pa_decode, pa_decode_partitioned, pa_decode_shared_prefix, pa_merge_partitions,
+               pa_prefill_varlen,
                pa_reshape_and_cache, pa_reshape_and_cache_varlen, pa_decode_balanced,
                pa_decode_workspace_size)
 
@@ -126,6 +127,15 @@ def run_decode_partitioned(d: DeviceWorkload, out: torch.Tensor, partition_size:
                           d.max_seq_len, float(d.w.scale), partition_size, tmp, ml, es,
                           d.k_scale, d.v_scale, d.alibi_slopes)
     pa_merge_partitions(out, tmp, ml, es, d.seq_lens, partition_size)
+    return tmp, ml, es
+
+
+def run_decode_shared_prefix(d: DeviceWorkload, out: torch.Tensor, shared_blocks: int,
+                             partition_size: int, bufs=None):
+    tmp, ml, es = bufs if bufs is not None else partial_buffers(d, partition_size)
+    pa_decode_shared_prefix(d.layout, out, d.q, d.k_cache, d.v_cache, d.block_table,
+                            d.seq_lens, d.max_seq_len, float(d.w.scale), shared_blocks,
+                            partition_size, tmp, ml, es, d.k_scale, d.v_scale, d.alibi_slopes)
     return tmp, ml, es
 
 

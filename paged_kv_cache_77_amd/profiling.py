@@ -48,16 +48,25 @@ RUNS = {
     "mixed_chunked_prefill": {
         "title": "mixed batch: 128 decode rows (contexts U[1024,8192]) + a 2048-token chunk on "
                  "a 6144-token prefix, 32 q / 8 KV heads, head_dim 128, bf16; step = fused write "
-                 "of 2176 tokens, then pa_prefill_varlen (decode kernel for the decode rows, "
-                 "MFMA prefill kernel for the chunk)",
+                 "of 2176 tokens, then pa_prefill_varlen (one launch: the chunk's MFMA "
+                 "prefill items, then the decode rows)",
         "args": "--config 4",
         "keys": {"config4_varlen": ["pa::varlen_kernel"],
                  "config4_prefill": ["pa::prefill_kernel"]},
     },
     "shared_prefix_fp8": {
         "title": "shared-prefix fp8 decode: 256 requests sharing 256 blocks (4096 tokens) + "
-                 "tails U[64,1024], 28 q / 4 KV heads, head_dim 128, fp8 e4m3 K/V",
+                 "tails U[64,1024], 28 q / 4 KV heads, head_dim 128, fp8 e4m3 K/V; "
+                 "pa_decode_shared_prefix (prefix partials on the matrix cores, tails by "
+                 "split-KV, merge)",
         "args": "--config 5",
+        "keys": {"config5_shared": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel",
+                                    "pa::merge_kernel"]},
+    },
+    "shared_prefix_fp8_per_request": {
+        "title": "the same workload through the per-request decode (pa_decode, matrix-core "
+                 "kernel)",
+        "args": "--config 5 --path single",
         "keys": {"config5_single": ["pa::decode_mfma_kernel"]},
     },
 }

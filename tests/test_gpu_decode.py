@@ -243,6 +243,70 @@ def test_full_size_config_sampled(cfg):
     check_bf16(dv.bits_of(out2)[sample], ref[sample], f"config {cfg} balanced")
 
 
+def _shared_case(case):
+    """(workload, shared_blocks, partition_size) for the shared-prefix cases."""
+    if case == "fp8_quarter_config5":          # 64 requests, 1024-token prefix, G = 7
+        w = wl.config_workload(5, scale_down=4)
+        return w, 64, 512
+    rng = np.random.default_rng(len(case))
+    if case == "bf16_alibi":                   # 40 requests on 2048 shared tokens
+        R, S = 40, 128
+        sl = [S * 16 + int(t) for t in rng.integers(1, 700, size=R)]
+        w = wl.make_workload(name="t", seq_lens=sl, q_lens=[1] * R, num_q_heads=32,
+                             num_kv_heads=8, head_dim=128, seed=91, writes_new_kv=False,
+                             shared_blocks=S, share=[S] * R, alibi=True, bt_extra_cols=2)
+        return w, S, 512
+    if case == "d64_short_requests":           # some requests end inside the prefix
+        R, S = 30, 64
+        sl = [S * 16 + int(t) for t in rng.integers(1, 300, size=R)]
+        sl[1:5] = [512, 1024, 16, 1040]           # request 0 holds the whole prefix
+        share = [min(S, x // 16) for x in sl]
+        w = wl.make_workload(name="t", seq_lens=sl, q_lens=[1] * R, num_q_heads=16,
+                             num_kv_heads=2, head_dim=64, seed=92, writes_new_kv=False,
+                             shared_blocks=S, share=share)
+        return w, S, 256
+    if case == "fp8_g1_no_prefix":             # shared_blocks 0: tails only
+        R = 12
+        sl = [int(t) for t in rng.integers(1, 900, size=R)]
+        w = wl.make_workload(name="t", seq_lens=sl, q_lens=[1] * R, num_q_heads=4,
+                             num_kv_heads=4, head_dim=128, seed=93, writes_new_kv=False,
+                             cache_dtype="fp8")
+        return w, 0, 128
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["fp8_quarter_config5", "bf16_alibi", "d64_short_requests",
+                                  "fp8_g1_no_prefix"])
+def test_decode_shared_prefix(case):
+    """pa_decode_shared_prefix (prefix partials on the matrix cores, tails by
+    split-KV, one merge) against the oracle on every row: query blocks that
+    end mid-block, requests shorter than the prefix (including one that ends
+    exactly where the prefix ends), ALiBi, and no prefix at all."""
+    _announce(f"shared-prefix decode {case}")
+    w, S, P = _shared_case(case)
+    d = dv.to_device(w)
+    out = _out(w)
+    dv.run_decode_shared_prefix(d, out, S, P)
+    torch.cuda.synchronize()
+    check_bf16(dv.bits_of(out), oracle.decode(w), f"shared prefix {case}")
+
+
+def test_decode_shared_prefix_full_config5_sampled():
+    """The shared-prefix workload at full size (256 requests, 4096 shared
+    tokens, fp8) in the launch configuration the benchmark times."""
+    _announce("shared-prefix decode, full config 5")
+    w = wl.config_workload(5)
+    d = dv.to_device(w)
+    out = _out(w)
+    dv.run_decode_shared_prefix(d, out, 256, 512)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    sample = sorted(set(rng.choice(w.num_reqs, size=8, replace=False).tolist())
+                    | {0, w.num_reqs - 1, int(np.argmax(w.seq_lens))})
+    ref = oracle.decode(w, requests=sample)
+    check_bf16(dv.bits_of(out)[sample], ref[sample], "config 5 shared prefix")
+
+
 def test_balanced_workspace_reuse_and_all_units_written():
     """Two calls in a row on one workspace (the second with fewer requests);
     every output row is written (NaN-prefilled outputs come back finite)."""
