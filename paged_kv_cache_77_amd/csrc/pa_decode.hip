@@ -322,6 +322,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const int r = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   int n = (seq_lens[r] + partition_size - 1) / partition_size;
   if (max_used > 0) n = min(n, max_used);      // the last record may be an open tail
+  n = min(n, max_num_partitions);              // (a seq_len past the host bound stays in bounds)
   const int64_t base = ((int64_t)r * num_q_heads + h) * max_num_partitions;
   const int pg = tid / TPR, c = tid % TPR;
 
@@ -380,6 +381,52 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const uint32_t w1 = (uint32_t)f32_to_bf16(sum.z * inv) | ((uint32_t)f32_to_bf16(sum.w * inv) << 16);
     *reinterpret_cast<uint2*>(out + ((int64_t)r * num_q_heads + h) * D + 4 * c) = make_uint2(w0, w1);
   }
+}
+
+// The same merge for short partition lists (at most kMergeFewParts per
+// request): one wave per (request, query head), four per work-group.  Lane p
+// holds partition p's weight l_p e^(m_p - m); every lane then sums its D/64
+// output elements over the partitions.
+constexpr int kMergeFewParts = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_few_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ tmp_out,
+    const float* __restrict__ max_logits, const float* __restrict__ exp_sums,
+    const int32_t* __restrict__ seq_lens, int32_t num_reqs, int32_t num_q_heads,
+    int32_t partition_size, int32_t max_num_partitions, int32_t max_used) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x % 64;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;     // r * Hq + h
+  if (unit >= (int64_t)num_reqs * num_q_heads) return;
+  const int r = (int)(unit / num_q_heads);
+  int n = (seq_lens[r] + partition_size - 1) / partition_size;
+  if (max_used > 0) n = min(n, max_used);      // the last record may be an open tail
+  n = min(n, max_num_partitions);              // (a seq_len past the host bound stays in bounds)
+  const int64_t base = unit * max_num_partitions;
+  const float m = lane < n ? max_logits[base + lane] : -INFINITY;
+  float M = m;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, xor_lanes(M, s));
+  const float wgt = (lane < n && m != -INFINITY) ? exp_sums[base + lane] * fast_exp2((m - M) * kLog2e)
+                                                 : 0.f;
+  float L = wgt;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) L += xor_lanes(L, s);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int p = 0; p < n; ++p) {
+    const float wp = __shfl(wgt, p, 64);
+    if (wp != 0.f) {                           // (a partition with no key holds no row)
+      const float* row = tmp_out + (base + p) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(wp, row[e], acc[e]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[unit * D + lane * E + e] = f32_to_bf16(acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -534,6 +581,20 @@ hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
                         int32_t max_num_partitions, hipStream_t st, int32_t max_used) {
   if (num_reqs == 0) return hipSuccess;
+  const int parts = max_used > 0 ? std::min(max_used, max_num_partitions) : max_num_partitions;
+  if (parts <= kMergeFewParts) {
+    const int64_t units = (int64_t)num_reqs * num_q_heads;
+    const dim3 g4((unsigned)((units + 3) / 4));
+    if (head_dim == 64)
+      hipLaunchKernelGGL(merge_few_kernel<64>, g4, dim3(256), 0, st, (uint16_t*)out, tmp_out,
+                         max_logits, exp_sums, seq_lens, num_reqs, num_q_heads, partition_size,
+                         max_num_partitions, max_used);
+    else
+      hipLaunchKernelGGL(merge_few_kernel<128>, g4, dim3(256), 0, st, (uint16_t*)out, tmp_out,
+                         max_logits, exp_sums, seq_lens, num_reqs, num_q_heads, partition_size,
+                         max_num_partitions, max_used);
+    return hipGetLastError();
+  }
   dim3 grid(num_q_heads, num_reqs);
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, st, (uint16_t*)out, tmp_out,
