@@ -303,8 +303,15 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     elif path == "shared":
         r["kernel"] = (f"pa_decode_shared_prefix: shared_prefix_kernel (MFMA, {shared} shared "
                        f"blocks) + {decode_kernel_name(w)} (tails, split-KV P={P}) + "
-                       "merge_kernel")
-        r["kbytes"] = nbytes["total"]
+                       "merge_few_kernel")
+        # the partial records (O, m, l per request, head and partition: the
+        # prefix's partitions plus one tail record), written and read back
+        first_tail = shared * 16 // P
+        recs = int(np.minimum((w.seq_lens.astype(np.int64) + P - 1) // P, first_tail + 1).sum())
+        part_bytes = 2 * recs * w.num_q_heads * (w.head_dim + 2) * 4
+        r["kbytes"] = nbytes["total"] + part_bytes
+        r["partials_bytes"] = part_bytes
+        nbytes = dict(nbytes, unique_total=nbytes["unique_total"] + part_bytes)
         r["shared_blocks"] = shared
     else:
         r["kernel"] = f"{decode_kernel_name(w)} (single pass)"

@@ -61,7 +61,7 @@ RUNS = {
                  "split-KV, merge)",
         "args": "--config 5",
         "keys": {"config5_shared": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel",
-                                    "pa::merge_kernel"]},
+                                    "pa::merge_few_kernel"]},
     },
     "shared_prefix_fp8_per_request": {
         "title": "the same workload through the per-request decode (pa_decode, matrix-core "
