@@ -53,6 +53,11 @@ RUNS = {
         "args": "--config 4",
         "keys": {"config4_varlen": ["pa::varlen_kernel"],
                  "config4_prefill": ["pa::prefill_kernel"]},
+        # matrix-core counters (derived metrics of rocprofv3): MfmaUtil = the
+        # share of SIMD cycles the MFMA pipe was busy, MfmaFlopsBF16 = bf16
+        # MFMA flops executed
+        "mfma": {"counters": ["MfmaUtil", "MfmaFlopsBF16"],
+                 "kernels": ["pa::prefill_kernel", "pa::varlen_kernel"]},
     },
     "shared_prefix_fp8": {
         "title": "shared-prefix fp8 decode: 256 requests sharing 256 blocks (4096 tokens) + "
@@ -62,6 +67,8 @@ RUNS = {
         "args": "--config 5",
         "keys": {"config5_shared": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel",
                                     "pa::merge_few_kernel"]},
+        "mfma": {"counters": ["MfmaUtil", "MfmaFlopsBF16", "MfmaFlopsF16"],
+                 "kernels": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel"]},
     },
     "shared_prefix_fp8_per_request": {
         "title": "the same workload through the per-request decode (pa_decode, matrix-core "
@@ -83,6 +90,9 @@ def commands(outdir: str = "gpurun_out/prof") -> list:
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             cmds.append(f"rocprofv3 --pmc {c} -d {outdir} -o {c.lower()}_{name} -- "
                         f"{BENCH} {r['args']} --steps 3 --warmup 1")
+        if "mfma" in r:
+            cmds.append(f"rocprofv3 --pmc {' '.join(r['mfma']['counters'])} -d {outdir} "
+                        f"-o mfma_{name} -- {BENCH} {r['args']} --steps 3 --warmup 1")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(f"rocprofv3 --pmc {c} -d {outdir} -o {c.lower()}_copy -- "
                     f"python3 bench.py --copy-calibration")
@@ -114,6 +124,23 @@ def _groups(db: str, counter: str = None) -> dict:
         for k in [k for k in out if k[1] is None]:
             dmax = max(d for d, _ in out[k])
             out[k] = [(d, v) for d, v in out[k] if d >= 0.5 * dmax]
+    con.close()
+    return out
+
+
+def _per_dispatch(db: str, counter: str) -> dict:
+    """(short name, grid) -> list of (duration ns, counter summed over the
+    dispatch's instances) -- rocprofv3 stores some derived counters once per
+    dispatch and others once per hardware instance."""
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    grids = {did: (gx, gy, gz) for did, gx, gy, gz in
+             cur.execute("select dispatch_id, grid_x, grid_y, grid_z from kernels")}
+    out = {}
+    rows = cur.execute("select name, dispatch_id, max(duration), sum(counter_value) from "
+                       "pmc_events where counter_name = ? group by dispatch_id", (counter,))
+    for n, did, d, v in rows:
+        out.setdefault((_short(n), grids.get(did)), []).append((d, v))
     con.close()
     return out
 
@@ -182,6 +209,20 @@ def summarize(outdir: str = "gpurun_out/prof", profiles: str = "profiles") -> di
             traffic[key] = {"bytes_per_launch": int(round(tot)), "kernel_sha": sha,
                             "kernels": prefixes}
             lines.append(f"# {key}: HBM traffic {tot / 1e6:.2f} MB per launch")
+        if "mfma" in r:
+            db = os.path.join(outdir, f"mfma_{name}_results.db")
+            lines.append("# matrix-core counters per dispatch (median over the group): "
+                         "MfmaUtil = % of SIMD cycles the MFMA pipe was busy, "
+                         "MfmaFlopsBF16 = bf16 MFMA flops executed")
+            vals = {c: _per_dispatch(db, c) for c in r["mfma"]["counters"]}
+            for pfx in r["mfma"]["kernels"]:
+                parts = []
+                for c, g in vals.items():
+                    k = _dominant(g, pfx)
+                    if k is not None:
+                        parts.append(f"{c} {statistics.median(v for _, v in g[k]):.4g}")
+                if parts:
+                    lines.append(f"{pfx:55s} " + "  ".join(parts))
         if bench_line is not None:
             rl = bench_line["roofline"]
             lines.append(f"# bench.py (same run, HIP events): kernel {rl['kernel_ms'] * 1e3:.3f} us, "

@@ -265,6 +265,13 @@ def _shared_case(case):
                              num_kv_heads=2, head_dim=64, seed=92, writes_new_kv=False,
                              shared_blocks=S, share=share)
         return w, S, 256
+    if case == "fp8_alibi":                    # 20 requests on 512 shared tokens, G = 7
+        R, S = 20, 32
+        sl = [S * 16 + int(t) for t in rng.integers(1, 400, size=R)]
+        w = wl.make_workload(name="t", seq_lens=sl, q_lens=[1] * R, num_q_heads=28,
+                             num_kv_heads=4, head_dim=128, seed=94, writes_new_kv=False,
+                             cache_dtype="fp8", shared_blocks=S, share=[S] * R, alibi=True)
+        return w, S, 256
     if case == "fp8_g1_no_prefix":             # shared_blocks 0: tails only
         R = 12
         sl = [int(t) for t in rng.integers(1, 900, size=R)]
@@ -276,7 +283,7 @@ def _shared_case(case):
 
 
 @pytest.mark.parametrize("case", ["fp8_quarter_config5", "bf16_alibi", "d64_short_requests",
-                                  "fp8_g1_no_prefix"])
+                                  "fp8_alibi", "fp8_g1_no_prefix"])
 def test_decode_shared_prefix(case):
     """pa_decode_shared_prefix (prefix partials on the matrix cores, tails by
     split-KV, one merge) against the oracle on every row: query blocks that
