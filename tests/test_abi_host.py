@@ -92,6 +92,32 @@ def test_partitioned_rejects_bad_partitioning():
     assert st(0, 8) == pa.PA_ERR_INVALID_ARG
 
 
+def test_shared_prefix_rejects_bad_arguments_without_launch():
+    """pa_decode_shared_prefix: partitions a multiple of 64 tokens, a prefix
+    of whole partitions within max_seq_len, enough partition slots, scratch
+    and output present and aligned -- all refused before any launch."""
+    L = pa.lib()
+    lay = pa.make_layout(64, 2, 128, 0)
+    p = ctypes.c_void_p(1024)
+
+    def st(shared=8, P=128, pmax=4, max_seq_len=400, tmp=p, out=p):
+        return L.pa_decode_shared_prefix(ctypes.byref(lay), out, p, 2, 8, p, p, p, 32, p,
+                                         max_seq_len, 0.1, None, None, None, shared, P, pmax,
+                                         tmp, p, p, None)
+    assert st(P=96) == pa.PA_ERR_INVALID_ARG              # not a multiple of 64
+    assert st(P=0) == pa.PA_ERR_INVALID_ARG
+    assert st(shared=6) == pa.PA_ERR_INVALID_ARG          # 96 tokens: not whole partitions
+    assert st(shared=-8) == pa.PA_ERR_INVALID_ARG
+    assert st(shared=32, P=256, max_seq_len=400) == pa.PA_ERR_INVALID_ARG   # 512 > 400
+    assert st(pmax=3) == pa.PA_ERR_INVALID_ARG            # 400 tokens need 4 partitions of 128
+    assert st(tmp=None) == pa.PA_ERR_INVALID_ARG
+    assert st(tmp=ctypes.c_void_p(1028)) == pa.PA_ERR_INVALID_ARG          # misaligned
+    assert st(out=None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_decode_shared_prefix(ctypes.byref(lay), None, None, 0, 8, None, None, None, 32,
+                                     None, 400, 0.1, None, None, None, 8, 128, 4, None, None,
+                                     None, None) == 0     # no requests: nothing to do
+
+
 def test_fp8_writes_need_scales():
     L = pa.lib()
     lay = pa.make_layout(10, 2, 128, 1)
