@@ -332,14 +332,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
     const int k0 = kt * kBN;
     if (k0 <= wave_pmax) {                      // some key of the tile is visible to the wave
       // -- S^T = K Q^T for the two 32-key halves of the tile
+      // (the two halves' MFMA chains interleaved: consecutive MFMAs are
+      // independent while the next K fragments are read)
       f32x16_t s[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[b][v] = 0.f;
-        const int key = 32 * b + lq;
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
+      for (int k = 0; k < KSTEPS; ++k) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int key = 32 * b + lq;
           const int c = 2 * k + lh;
           const uint4 kf = sm.k[buf][key * CH + (c ^ (key & (CH - 1)))];
           s[b] = mfma32(kf, qf[k], s[b]);
@@ -420,9 +424,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
         const int G = lane / 16, gi = lane % 16;
         const char* vbuf = reinterpret_cast<const char*>(&sm.vt[buf][0]);
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
+        for (int ks = 0; ks < 4; ++ks) {             // (d blocks' chains interleaved)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
+          for (int db = 0; db < DBLK; ++db) {
             const int r0 = 32 * (ks / 2) + 16 * (ks % 2) + 4 * lh + gi / 4;
             const int e0 = 32 * db + 16 * (G & 1) + 4 * (gi % 4);
             uint2 part[2];
