@@ -2,11 +2,14 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
 One step = one pass of the hot path over one batch: slot mapping of the
-step's new tokens and their scatter into the paged cache (one fused launch),
-then paged decode attention over every request (split-KV + merge, or a
-single pass), for the batched-decode workload (64 requests, contexts
-uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
-16-token blocks, one layer).  Other workloads are selected with --config.
+step's new tokens and their scatter into the paged cache, then paged decode
+attention over every request, for the batched-decode workload (64 requests,
+contexts uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
+16-token blocks, one layer): one pa_decode_append call, whose decode
+work-groups write the new rows before they read.  Other workloads are
+selected with --config (split-KV + merge for the long contexts, the
+shared-prefix decode, the mixed chunked-prefill batch); --path single times
+the write and pa_decode as two launches.
 
 Prints ONE JSON line.  value = algorithmic decode bytes (K and V read once
 per KV head, plus Q, O, block-table entries and seq_lens) per second of
@@ -161,7 +164,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     d = dv.to_device(w, "cuda")
     nbytes = decode_bytes(w)
     if path == "auto":
-        path = {3: "split", 5: "shared"}.get(cfg, "single")
+        path = {3: "split", 5: "shared"}.get(cfg, "append" if cfg in (1, 2) else "single")
     P = partition_size or (w.partition_size if cfg in (3, 5) else 1024)
     shared = shared_prefix_blocks(w, P) if path == "shared" else 0
     is_prefill = cfg == 4
@@ -180,6 +183,8 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
             dv.run_prefill(d, out)
         elif path == "single":
             dv.run_decode(d, out)
+        elif path == "append":
+            dv.run_decode_append(d, out, sm[:T])     # write + decode, one call
         elif path == "balanced":
             dv.run_decode_balanced(d, out, ws)
         elif path == "shared":
@@ -191,7 +196,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
                                      es, d.k_scale, d.v_scale)
 
     def step(timed: bool):
-        if w.writes_new_kv:
+        if w.writes_new_kv and path != "append":
             dv.write_new_kv_fused(d, sm[:T])      # slot mapping + scatter, one launch
         e0 = e1 = None
         if timed:
@@ -211,9 +216,13 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(True)
+        step(False)            # the timed steps carry no event markers of their own
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # the same steps again with an event pair around each attention call
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
     warm = sorted(a.elapsed_time(b) for a, b in ev)
 
     # Kernel time: a train of back-to-back attention calls between two
@@ -313,6 +322,12 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
         r["partials_bytes"] = part_bytes
         nbytes = dict(nbytes, unique_total=nbytes["unique_total"] + part_bytes)
         r["shared_blocks"] = shared
+    elif path == "append":
+        r["kernel"] = (f"{decode_kernel_name(w)} (single pass, writing each request's new "
+                       "K/V row first)")
+        # + the new rows written (K and V, every KV head)
+        eb = 1 if w.cache_dtype == "fp8" else 2
+        r["kbytes"] = nbytes["total"] + 2 * w.num_reqs * w.num_kv_heads * w.head_dim * eb
     else:
         r["kernel"] = f"{decode_kernel_name(w)} (single pass)"
         r["kbytes"] = nbytes["total"]
@@ -418,11 +433,14 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", choices=["auto", "split", "single", "balanced", "shared"],
+    ap.add_argument("--path", choices=["auto", "split", "single", "balanced", "shared",
+                                       "append"],
                     default="auto",
                     help="decode path; auto = split-KV for the long-context workload, the "
-                         "shared-prefix decode for the shared-prefix workload, single pass "
-                         "otherwise (measured faster for these batches)")
+                         "shared-prefix decode for the shared-prefix workload, the single "
+                         "pass with the step's write in the same call (pa_decode_append) "
+                         "for the decode workloads that write new tokens, single pass "
+                         "otherwise")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV partition size in tokens (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -496,6 +514,10 @@ def main() -> int:
         # the shared-prefix workload through the per-request decode (pa_decode)
         o = measure(5, "single", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
         other["config5_per_request_decode"] = summary(o)
+        del o
+        # the batched-decode step as two launches (write, then pa_decode)
+        o = measure(2, "single", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
+        other["config2_write_then_decode"] = summary(o)
         del o
         other["block_manager"] = block_manager_rate()
         res["other_workloads"] = other

@@ -178,6 +178,29 @@ int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int
                        size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step with its write: each request's newest token -- position
+ * seq_lens[r] - 1, its slot block_table[r][pos / 16] * 16 + pos % 16 (P1
+ * §3.1) -- gets key[r] / value[r] written into the pools (P3's
+ * reshape_and_cache; FP8 pools quantised as pa_reshape_and_cache does),
+ * then pa_decode runs over the contexts that now include it.  Same pools
+ * and output as pa_reshape_and_cache with that slot mapping followed by
+ * pa_decode.  Where the vector-ALU decode runs with one head chunk per KV
+ * head (bf16 caches with GQA groups up to 7, FP8 caches with groups up to
+ * 3), the write happens inside the decode's own work-groups (one launch);
+ * otherwise it is a launch of its own before the decode.
+ *  key, value    : bf16 [num_reqs][num_kv_heads][head_dim], one row per request
+ *  slot_mapping  : int64 [num_reqs], written with each request's slot (NULL: not written)
+ *  k_cache, v_cache : written (the token's row), then read
+ * Other arguments as pa_decode; every seq_len must be >= 1.
+ */
+int pa_decode_append(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                     int32_t num_q_heads, void* k_cache, void* v_cache, const void* key,
+                     const void* value, int64_t* slot_mapping, const int32_t* block_table,
+                     int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                     float scale, const float* k_scale, const float* v_scale,
+                     const float* alibi_slopes, void* stream);
+
+/*
  * Split-KV decode, first stage (P1 §3.2.7 and §3.3, the V2 partitioning).
  * Partition p of request r covers tokens [p*P, min((p+1)*P, seq_len)).
  * For every partition p < ceil(seq_lens[r]/P) and query head h writes

@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
     "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
-    "pa_decode_shared_prefix",
+    "pa_decode_shared_prefix", "pa_decode_append",
     # host block manager (include/pa_blocks.h; binding in blocks.py)
     "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
     "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
             "pa_merge_partitions": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
             "pa_decode_partitioned_range": ([lp, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
                                              _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+            "pa_decode_append": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _F,
+                                  _P, _P, _P, _P], _I),
             "pa_decode_shared_prefix": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P,
                                          _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
             "pa_prefill_varlen": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -269,6 +271,18 @@ def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,
         _dev(exp_sums, "exp_sums"), _dev(seq_lens, "seq_lens"), seq_lens.shape[0],
         out.shape[1], out.shape[2], int(partition_size), max_logits.shape[2], _stream()),
         "pa_merge_partitions")
+
+
+def pa_decode_append(layout, out, q, k_cache, v_cache, key, value, slot_mapping, block_table,
+                     seq_lens, max_seq_len: int, scale: float, k_scale=None, v_scale=None,
+                     alibi_slopes=None) -> None:
+    _check(lib().pa_decode_append(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(key, "key"),
+        _dev(value, "value"), _dev(slot_mapping, "slot_mapping"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"),
+        _stream()), "pa_decode_append")
 
 
 def pa_decode_shared_prefix(layout, out, q, k_cache, v_cache, block_table, seq_lens,

@@ -209,6 +209,27 @@ int pa_decode_balanced(const pa_kv_layout* layout, void* out, const void* q, int
   return hip_status(pa::launch_decode_balanced(a, workspace, (hipStream_t)stream));
 }
 
+int pa_decode_append(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                     int32_t num_q_heads, void* k_cache, void* v_cache, const void* key,
+                     const void* value, int64_t* slot_mapping, const int32_t* block_table,
+                     int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                     float scale, const float* k_scale, const float* v_scale,
+                     const float* alibi_slopes, void* stream) {
+  PA_TRY(decode_common(layout, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                       bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale));
+  if (num_reqs == 0) return PA_OK;
+  if (!out || !aligned16(out) || !key || !value || !aligned16(key) || !aligned16(value))
+    return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a = decode_args(layout, q, num_reqs, num_q_heads, k_cache, v_cache,
+                                 block_table, bt_stride, seq_lens, max_seq_len, scale, k_scale,
+                                 v_scale, alibi_slopes);
+  a.out = out;
+  a.new_k = key;
+  a.new_v = value;
+  a.slot_out = slot_mapping;
+  return hip_status(pa::launch_decode_append(a, (hipStream_t)stream));
+}
+
 int pa_decode_partitioned(const pa_kv_layout* layout, const void* q, int32_t num_reqs,
                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int32_t bt_stride,

@@ -40,25 +40,6 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
   return hipGetLastError();
 }
 
-// Store 8 source elements (one 16-byte chunk of bf16) at chunk index `dst`
-// of the pool: a bit copy for bf16 pools, 8 quantised codes for FP8 pools.
-template <bool FP8>
-__device__ __forceinline__ void store_chunk(void* pool, int64_t dst, const uint4& src,
-                                            float scale) {
-  if constexpr (!FP8) {
-    reinterpret_cast<uint4*>(pool)[dst] = src;
-  } else {
-    const uint32_t w[4] = {src.x, src.y, src.z, src.w};
-    uint32_t c[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = (e & 1) ? bf16hi(w[e / 2]) : bf16lo(w[e / 2]);
-      c[e / 4] |= f32_to_fp8_e4m3fn(div_rn(x, scale)) << (8 * (e % 4));
-    }
-    reinterpret_cast<uint2*>(pool)[dst] = make_uint2(c[0], c[1]);
-  }
-}
-
 // One thread per 16-byte chunk of a (token, KV head) source row, K and V
 // together.  Rows are head_dim bf16 = 8 or 16 chunks; a tile row in the pool
 // holds the same head_dim elements in order, so chunk c of the source lands
@@ -83,6 +64,50 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const float ks = FP8 ? *k_scale : 1.f, vs = FP8 ? *v_scale : 1.f;
   store_chunk<FP8>(k_cache, dst, key[i], ks);
   store_chunk<FP8>(v_cache, dst, value[i], vs);
+}
+
+// The newest token of every request (position seq_len - 1), all KV heads:
+// one work-group per request, one thread per 16-byte source chunk.
+template <bool FP8>
+__global__ __launch_bounds__(256) void append_rows_kernel(
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const uint4* __restrict__ key,
+    const uint4* __restrict__ value, const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const int32_t* __restrict__ seq_lens, int32_t num_kv_heads, int32_t head_dim,
+    int64_t* __restrict__ slot_out, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  const int r = blockIdx.x;
+  const int L = seq_lens[r];
+  if (L <= 0) return;                                  // no token in this step
+  const int pos = L - 1;
+  const int64_t slot = (int64_t)block_table[(int64_t)r * bt_stride + pos / kBlock] * kBlock +
+                       pos % kBlock;
+  if (threadIdx.x == 0 && slot_out != nullptr) slot_out[r] = slot;
+  const int chunks = head_dim / 8;
+  const float ks = FP8 ? *k_scale : 1.f, vs = FP8 ? *v_scale : 1.f;
+  for (int i = threadIdx.x; i < num_kv_heads * chunks; i += blockDim.x) {
+    const int g = i / chunks, c = i - g * chunks;
+    const int64_t dst = slot_offset(slot, g, num_kv_heads, head_dim) / 8 + c;
+    const int64_t src = (int64_t)r * num_kv_heads * chunks + i;
+    store_chunk<FP8>(k_cache, dst, key[src], ks);
+    store_chunk<FP8>(v_cache, dst, value[src], vs);
+  }
+}
+
+hipError_t launch_append_rows(void* k_cache, void* v_cache, const void* key, const void* value,
+                              const int32_t* block_table, int32_t bt_stride,
+                              const int32_t* seq_lens, int32_t num_reqs, int32_t num_kv_heads,
+                              int32_t head_dim, int64_t* slot_out, bool fp8,
+                              const float* k_scale, const float* v_scale, hipStream_t stream) {
+  if (num_reqs == 0) return hipSuccess;
+  if (fp8)
+    hipLaunchKernelGGL(append_rows_kernel<true>, dim3(num_reqs), dim3(256), 0, stream, k_cache,
+                       v_cache, (const uint4*)key, (const uint4*)value, block_table, bt_stride,
+                       seq_lens, num_kv_heads, head_dim, slot_out, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(append_rows_kernel<false>, dim3(num_reqs), dim3(256), 0, stream, k_cache,
+                       v_cache, (const uint4*)key, (const uint4*)value, block_table, bt_stride,
+                       seq_lens, num_kv_heads, head_dim, slot_out, k_scale, v_scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key,

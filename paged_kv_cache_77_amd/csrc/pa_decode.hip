@@ -563,6 +563,29 @@ hipError_t launch_decode(const DecodeArgs& a, bool partitioned, hipStream_t st) 
   return launch_any(a, partitioned ? 1 : 0, nullptr, st);
 }
 
+hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st) {
+  if (a.num_reqs == 0) return hipSuccess;
+  const bool fp8 = a.cache_dtype != 0;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  // the vector-ALU single pass with one head chunk per KV head writes the
+  // rows itself; the other paths get them from a launch before
+  const bool in_kernel = !(PA_DECODE_FP8_MFMA && fp8 && G >= 4) &&
+                         !(PA_DECODE_BF16_MFMA_MIN_G > 0 && !fp8 &&
+                           G >= PA_DECODE_BF16_MFMA_MIN_G) &&
+                         G <= 8;
+  if (in_kernel) return launch_any(a, 0, nullptr, st);
+  const hipError_t e = launch_append_rows(const_cast<void*>(a.k_cache),
+                                          const_cast<void*>(a.v_cache), a.new_k, a.new_v,
+                                          a.block_table, a.bt_stride, a.seq_lens, a.num_reqs,
+                                          a.num_kv_heads, a.head_dim, a.slot_out, fp8, a.k_scale,
+                                          a.v_scale, st);
+  if (e != hipSuccess) return e;
+  DecodeArgs b = a;
+  b.new_k = b.new_v = nullptr;
+  b.slot_out = nullptr;
+  return launch_any(b, 0, nullptr, st);
+}
+
 hipError_t launch_decode_balanced(const DecodeArgs& a, void* workspace, hipStream_t st) {
   return launch_any(a, 2, workspace, st);
 }

@@ -608,6 +608,32 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, DecodeSmem<D, G
     return;
   }
 
+  if constexpr (!PART) {
+    // append mode (one head chunk per KV head): this work-group writes its KV
+    // head's row of the request's newest token (position seq_len - 1,
+    // P3's slot formula) and is the only one to read that head's tiles of
+    // the request, so a block-level release and barrier order the write
+    // before the loads below
+    if (a.new_k != nullptr) {
+      const int pos = seq_len - 1;
+      const int64_t slot =
+          (int64_t)a.block_table[(int64_t)r * a.bt_stride + pos / kBlock] * kBlock + pos % kBlock;
+      constexpr int CHK = D / 8;                  // 16-byte source chunks per row
+      if (tid < 2 * CHK) {
+        const bool is_v = tid >= CHK;
+        const int c = tid - (is_v ? CHK : 0);
+        const uint4 src = reinterpret_cast<const uint4*>(is_v ? a.new_v : a.new_k)
+            [((int64_t)r * a.num_kv_heads + g) * CHK + c];
+        const float qs = FP8 ? *(is_v ? a.v_scale : a.k_scale) : 1.f;
+        store_chunk<FP8>(const_cast<void*>(is_v ? a.v_cache : a.k_cache),
+                         slot_offset(slot, g, a.num_kv_heads, D) / 8 + c, src, qs);
+      }
+      if (g == 0 && tid == 0 && a.slot_out != nullptr) a.slot_out[r] = slot;
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
+
   float qk_scale = a.scale * kLog2e;
   if constexpr (FP8) qk_scale *= *a.k_scale;
   Dec dec;

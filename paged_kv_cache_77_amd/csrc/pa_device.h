@@ -122,6 +122,25 @@ __device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_
 }
 
 // ---------------------------------------------------------------------------
+// Store 8 source elements (one 16-byte chunk of bf16) at chunk index `dst`
+// of the pool: a bit copy for bf16 pools, 8 quantised codes for FP8 pools.
+template <bool FP8>
+__device__ __forceinline__ void store_chunk(void* pool, int64_t dst, const uint4& src,
+                                            float scale) {
+  if constexpr (!FP8) {
+    reinterpret_cast<uint4*>(pool)[dst] = src;
+  } else {
+    const uint32_t w[4] = {src.x, src.y, src.z, src.w};
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? bf16hi(w[e / 2]) : bf16lo(w[e / 2]);
+      c[e / 4] |= f32_to_fp8_e4m3fn(div_rn(x, scale)) << (8 * (e % 4));
+    }
+    reinterpret_cast<uint2*>(pool)[dst] = make_uint2(c[0], c[1]);
+  }
+}
+
 // cross-lane moves (DPP within 16-lane rows; ds_bpermute across rows)
 
 template <int kCtrl>

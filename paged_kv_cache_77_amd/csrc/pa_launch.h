@@ -18,6 +18,9 @@ struct DecodeArgs {
   const float* v_scale;
   const float* alibi_slopes;        // fp32 [num_q_heads] or NULL (no bias)
   void* out;                        // bf16, final output (NULL in partitioned mode)
+  const void* new_k;                // append mode: this step's K/V rows [R][Hkv][D] bf16,
+  const void* new_v;                //   written at position seq_len - 1 before decoding
+  int64_t* slot_out;                // append mode: each request's slot (or NULL)
   float* tmp_out;                   // partitioned mode only
   float* max_logits;
   float* exp_sums;
@@ -43,6 +46,20 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* ke
                                     const int64_t* slot_mapping, int32_t num_kv_heads,
                                     int32_t head_dim, bool fp8, const float* k_scale,
                                     const float* v_scale, hipStream_t stream);
+
+// Each request's newest token (position seq_len - 1) from key/value [R][Hkv][D]
+// bf16 into the pools at its slot (quantised for FP8 pools); slot_out[r]
+// gets the slot when given.  One work-group per request.
+hipError_t launch_append_rows(void* k_cache, void* v_cache, const void* key, const void* value,
+                              const int32_t* block_table, int32_t bt_stride,
+                              const int32_t* seq_lens, int32_t num_reqs, int32_t num_kv_heads,
+                              int32_t head_dim, int64_t* slot_out, bool fp8,
+                              const float* k_scale, const float* v_scale, hipStream_t stream);
+
+// Decode with the append: the newest token's K/V written first (in the
+// decode kernel's own work-groups where the path allows, else one more
+// launch before it).
+hipError_t launch_decode_append(const DecodeArgs& args, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache_varlen(void* k_cache, void* v_cache, const void* key,
                                            const void* value, const int32_t* block_table,

@@ -10,7 +10,8 @@ import numpy as np
 import torch
 
 from . import (PA_CACHE_BF16, PA_CACHE_FP8_E4M3, make_layout, pa_compute_slot_mapping,
-               pa_decode, pa_decode_partitioned, pa_decode_shared_prefix, pa_merge_partitions,
+               pa_decode, pa_decode_append, pa_decode_partitioned, pa_decode_shared_prefix,
+               pa_merge_partitions,
                pa_prefill_varlen,
                pa_reshape_and_cache, pa_reshape_and_cache_varlen, pa_decode_balanced,
                pa_decode_workspace_size)
@@ -100,6 +101,14 @@ def write_new_kv_fused(d: DeviceWorkload, slot_mapping: Optional[torch.Tensor] =
     pa_reshape_and_cache_varlen(d.layout, d.k_cache, d.v_cache, d.k_new, d.v_new,
                                 d.block_table, d.query_start_loc, d.seq_lens, slot_mapping,
                                 d.k_scale, d.v_scale)
+
+
+def run_decode_append(d: DeviceWorkload, out: torch.Tensor,
+                      slot_mapping: Optional[torch.Tensor] = None) -> None:
+    """One decode step with its write (each request's new row, then decode)."""
+    pa_decode_append(d.layout, out, d.q, d.k_cache, d.v_cache, d.k_new, d.v_new, slot_mapping,
+                     d.block_table, d.seq_lens, d.max_seq_len, float(d.w.scale), d.k_scale,
+                     d.v_scale, d.alibi_slopes)
 
 
 def run_decode(d: DeviceWorkload, out: torch.Tensor) -> None:

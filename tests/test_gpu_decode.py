@@ -159,6 +159,57 @@ def test_decode_wide_ranked_batches(R, hq, hkv, d, ctx_hi, alibi):
     assert np.all(bits[empty] == 0)
 
 
+@pytest.mark.parametrize("hq,hkv,d,cache,alibi", [
+    (32, 8, 128, "bf16", False), (16, 8, 64, "bf16", True), (28, 4, 128, "bf16", False),
+    (4, 4, 128, "fp8", False), (28, 4, 128, "fp8", True), (64, 8, 128, "bf16", False)])
+def test_decode_append(hq, hkv, d, cache, alibi):
+    """pa_decode_append: each request's newest K/V row written at its slot,
+    then decode -- the pools bit for bit as the oracle's scatter leaves them
+    (including every untouched, NaN-poisoned slot), the slot mapping, and the
+    output against the oracle.  Groups below 8 on bf16 and below 4 on fp8
+    write inside the decode work-groups; the others take the launch before."""
+    _announce(f"decode append hq={hq} hkv={hkv} d={d} {cache} alibi={alibi}")
+    ctx = [1, 16, 17, 33, 100, 513, 2049, 1500, 700, 64] * 4
+    w = wl.make_workload(name="t", seq_lens=ctx, q_lens=[1] * len(ctx), num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, seed=95 + hq + d, cache_dtype=cache,
+                         writes_new_kv=True, alibi=alibi, bt_extra_cols=2)
+    dd = dv.to_device(w)
+    sm = torch.full((w.num_reqs,), -7, dtype=torch.int64, device="cuda")
+    out = _out(w)
+    dv.run_decode_append(dd, out, sm)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    assert np.array_equal(sm.cpu().numpy(), ref_sm)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16,
+                                      cache_dtype=w.cache_dtype, k_scale=w.k_scale,
+                                      v_scale=w.v_scale)
+    got_k = dv.bits_of(dd.k_cache) if cache == "bf16" else dd.k_cache.cpu().numpy()
+    got_v = dv.bits_of(dd.v_cache) if cache == "bf16" else dd.v_cache.cpu().numpy()
+    assert np.array_equal(got_k, kp) and np.array_equal(got_v, vp), "pools after the append"
+    check_bf16(dv.bits_of(out), oracle.decode(w, k_pool=kp, v_pool=vp), "decode append")
+
+
+def test_decode_append_full_config2_sampled():
+    """The batched-decode workload's step as one call, in the benchmark's
+    launch configuration: pools bit-exact, sampled rows against the oracle."""
+    _announce("decode append, full config 2")
+    w = wl.config_workload(2)
+    d = dv.to_device(w)
+    sm = torch.empty((w.num_reqs,), dtype=torch.int64, device="cuda")
+    out = _out(w)
+    dv.run_decode_append(d, out, sm)
+    torch.cuda.synchronize()
+    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    assert np.array_equal(sm.cpu().numpy(), ref_sm)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
+    assert np.array_equal(dv.bits_of(d.k_cache), kp) and np.array_equal(dv.bits_of(d.v_cache), vp)
+    rng = np.random.default_rng(22)
+    sample = sorted(set(rng.choice(w.num_reqs, size=6, replace=False).tolist())
+                    | {int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))})
+    ref = oracle.decode(w, k_pool=kp, v_pool=vp, requests=sample)
+    check_bf16(dv.bits_of(out)[sample], ref[sample], "config 2 append")
+
+
 def test_decode_empty_context_is_zero():
     _announce("decode seq_len 0")
     w = wl.make_workload(name="t", seq_lens=[0, 20], q_lens=[0, 0], num_q_heads=4,
