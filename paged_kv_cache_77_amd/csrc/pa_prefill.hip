@@ -21,8 +21,8 @@
 //       reductions are in-lane plus one swap with lane^32)
 //   O^T[d x 32 queries] += V^T . P^T      (P^T comes straight from the S^T
 //       accumulators: the MFMA contraction order over keys is permuted to the
-//       order the accumulators hold them, and V^T is stored in LDS in that
-//       order)
+//       order the accumulators hold them, and the V^T fragments are read
+//       from LDS in that order)
 // bf16 caches: each wave copies one 16-token block of K and of V straight
 // from global memory into LDS (global_load_lds_dwordx4: no staging
 // registers), both row-major with a 16-byte-chunk XOR swizzle; the V^T
