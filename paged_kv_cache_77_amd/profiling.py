@@ -34,10 +34,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 RUNS = {
     "batched_decode": {
         "title": "batched decode: 64 requests, contexts U[512,4096], 32 q / 8 KV heads, "
-                 "head_dim 128, bf16; step = fused slot mapping + scatter of 64 tokens, then "
-                 "single-pass decode",
+                 "head_dim 128, bf16; step = pa_decode_append (each request's new K/V row "
+                 "written by its decode work-groups, then the single-pass decode), one launch",
         "args": "--config 2",
-        "keys": {"config2_single": ["pa::decode_kernel"]},
+        "keys": {"config2_append": ["pa::decode_kernel"]},
     },
     "long_context_split": {
         "title": "long-context split-KV decode: 8 requests x 32768 tokens, 32 q / 8 KV heads, "
