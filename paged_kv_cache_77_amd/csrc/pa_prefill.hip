@@ -29,8 +29,8 @@
 // fragments of the PV products come from gfx950's transposing LDS read
 // (ds_read_b64_tr_b16).  FP8 caches are converted to bf16 in registers on
 // the way and stored in the same layout.  All tiles are double-buffered.
-// P^T enters the PV products as a bf16 high part plus a bf16 remainder (two
-// MFMAs per V^T fragment), so the probabilities keep ~16 significant bits.
+// P^T enters the PV products in bf16, and the softmax denominator sums those
+// same rounded weights, so O stays an exact weighted average of V's rows.
 #include <algorithm>
 
 #include "pa_decode_wave.h"
@@ -388,30 +388,28 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
           for (int v = 0; v < 16; ++v) oacc[b][v] *= alpha;
       }
       // -- P^T as bf16 B operands: k-step (b, s') takes accumulator rows
-      // 8s'..8s'+7.  Each probability is split into a bf16 high part (pf) and
-      // the bf16 of the remainder (pl), both multiplied into O^T, so the
-      // weights keep ~16 significant bits: one bf16 rounding (2^-9 relative)
-      // times |v| of a few units would otherwise take a peaked softmax's
-      // output near the 1e-2 bound.
-      uint4 pf[4], pl[4];
+      // 8s'..8s'+7.  The row sum l takes the same bf16-rounded weights that
+      // multiply V, so O = sum(p~ v) / sum(p~) is an exact weighted average:
+      // a rounding (2^-9 relative per weight) moves O by at most 2^-9 times
+      // the spread of v about O, and a one-hot row gives its v exactly.
+      // (Summing the unrounded p instead leaves a bias of the same order
+      // times |v|, which took peaked rows past the tolerance.)
+      uint4 pf[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
           float p[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < 8; ++e)
             p[e] = fast_exp2(fmaf(s[b][8 * sp + e], sc, -m_run));   // -inf -> 0
-            l_run += p[e];
-          }
-          uint32_t hw[4], lw[4];
+          uint32_t hw[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             hw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-            lw[e] = pack_bf16x2(p[2 * e] - bf16lo(hw[e]), p[2 * e + 1] - bf16hi(hw[e]));
+            l_run += bf16lo(hw[e]) + bf16hi(hw[e]);
           }
           pf[2 * b + sp] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          pl[2 * b + sp] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
       // -- O^T += V^T P^T
       {
@@ -438,7 +436,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
             }
             const uint4 vf = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
             oacc[db] = mfma32(vf, pf[ks], oacc[db]);
-            oacc[db] = mfma32(vf, pl[ks], oacc[db]);
           }
         }
       }
