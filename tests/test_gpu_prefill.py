@@ -170,3 +170,28 @@ def test_prefill_fp8_cache_with_new_tokens():
                          cache_dtype="fp8", **MIX)
     got, kp, vp = _run(w)
     check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "prefill fp8 + write")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_prefill_zero_query_is_causal_mean(cache):
+    """Q = 0: every visible weight is exp(0) = 1, exact in any precision, so
+    query i's output is the plain mean of V over keys 0..p_i (a closed form,
+    computed here from the gathered cache rows, not from the oracle's
+    softmax).  Checks the causal window, the partial last tile and that the
+    softmax denominator counts exactly the weights multiplied into V."""
+    _announce(f"prefill zero query {cache}")
+    w = wl.make_workload(name="t", seq_lens=[300, 129, 2000, 65], q_lens=[300, 64, 500, 65],
+                         num_q_heads=8, num_kv_heads=2, head_dim=128, seed=48,
+                         cache_dtype=cache, writes_new_kv=False, zero_q=True)
+    got, _, _ = _run(w, write=False)
+    vals = oracle.cache_values(w.v_pool, w.cache_dtype, float(w.v_scale))
+    ref = np.full((w.num_tokens, w.num_q_heads, w.head_dim), np.nan)
+    for r in range(w.num_reqs):
+        L, ql = int(w.seq_lens[r]), int(w.q_lens[r])
+        V = oracle.gather_kv(vals, w.block_table[r], L, 16)          # [L, Hkv, d]
+        cum = np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None, None]
+        row0 = int(w.query_start_loc[r])
+        for i, p in enumerate(oracle.token_positions(L, ql)):
+            for h in range(w.num_q_heads):
+                ref[row0 + i, h] = cum[p, h // w.group_size]
+    check_bf16(got, ref, f"prefill zero query {cache}")
