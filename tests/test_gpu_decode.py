@@ -87,7 +87,7 @@ def test_decode_shapes(hq, hkv, d, cache):
 
 
 def test_decode_long_single_pass_and_boosted_rows():
-    """A 10k-token context in one pass (block-table reload path) with the
+    """A 10k-token context in one pass with the
     x8 rows that force the running max to move."""
     _announce("decode long single pass")
     w = wl.make_workload(name="t", seq_lens=[10000, 4097, 1], q_lens=[1, 1, 1], num_q_heads=32,
@@ -105,6 +105,29 @@ def test_decode_long_single_pass_and_boosted_rows():
     check_bf16(dv.bits_of(out), ref, "single pass")
     check_bf16(dv.bits_of(out2), ref, "split-KV")
     check_bf16(dv.bits_of(out3), ref, "balanced")
+
+
+@pytest.mark.parametrize("hq,hkv,cache,alibi", [
+    (32, 8, "bf16", False),     # vector kernel
+    (28, 4, "fp8", True),       # matrix-core kernel, f16 products
+    (64, 8, "bf16", False)])    # matrix-core kernel, bf16 products
+def test_decode_single_pass_crosses_table_chunks(hq, hkv, cache, alibi):
+    """Contexts past 1024 blocks (16384 tokens) in one pass: the block-table
+    range is staged in LDS 1024 entries at a time, so these walk two chunks
+    (20000 tokens: a partial second chunk; 16400: one block past the first)."""
+    _announce(f"decode past one table chunk hq={hq} hkv={hkv} {cache} alibi={alibi}")
+    w = wl.make_workload(name="t", seq_lens=[20000, 16400, 16384, 3], q_lens=[1] * 4,
+                         num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seed=35 + hq,
+                         cache_dtype=cache, writes_new_kv=False, alibi=alibi, bt_extra_cols=1)
+    d = dv.to_device(w)
+    out = _out(w)
+    dv.run_decode(d, out)
+    out2 = _out(w)
+    dv.run_decode_partitioned(d, out2, 4096)
+    torch.cuda.synchronize()
+    ref = oracle.decode(w)
+    check_bf16(dv.bits_of(out), ref, "single pass")
+    check_bf16(dv.bits_of(out2), ref, "split-KV, 4096-token partitions")
 
 
 @pytest.mark.parametrize("ctx_hi,cache", [(700, "bf16"), (1900, "bf16"), (1900, "fp8")])
