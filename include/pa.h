@@ -382,6 +382,20 @@ int pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* strea
 int pa_debug_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream);
 
 /*
+ * Measurement support (not part of the attention path): read `bytes` (a
+ * multiple of 16) of device memory at `src` (16-byte aligned) once, as a
+ * grid-strided stream of 16-byte non-temporal loads (eight in flight per
+ * thread) by `work_groups` 256-thread work-groups (<= 0: eight per compute
+ * unit), enqueued on `stream`.  The caller times it: bytes / time is the
+ * device's streaming-read rate, the ceiling the decode kernels' HBM rates
+ * are compared with besides the published peak.  sink: one device uint32,
+ * written only if some thread's data XOR to 0xffffffff (it keeps the loads
+ * from being removed).
+ */
+int pa_measure_read_stream(const void* src, size_t bytes, uint32_t* sink, int32_t work_groups,
+                           void* stream);
+
+/*
  * Host-side check of metadata the kernels trust.  All arrays are HOST
  * pointers.  Checks: query_start_loc starts at 0 and is non-decreasing;
  * 0 <= q_len <= seq_len; seq_len <= bt_stride*block_size; every block-table

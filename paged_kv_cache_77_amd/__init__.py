@@ -22,7 +22,7 @@ __all__ = [
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
     "PaDecodePlan", "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
-    "EXPORTED_SYMBOLS",
+    "pa_decode_shared_prefix", "pa_decode_append", "pa_measure_read_stream", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "pa_decode_partitioned", "pa_merge_partitions", "pa_prefill_varlen",
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
     "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
-    "pa_decode_shared_prefix", "pa_decode_append",
+    "pa_decode_shared_prefix", "pa_decode_append", "pa_measure_read_stream",
     # host block manager (include/pa_blocks.h; binding in blocks.py)
     "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
     "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
                                              _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
             "pa_decode_append": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _I, _F,
                                   _P, _P, _P, _P], _I),
+            "pa_measure_read_stream": ([_P, ctypes.c_size_t, _P, _I, _P], _I),
             "pa_decode_shared_prefix": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P,
                                          _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
             "pa_prefill_varlen": ([lp, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -283,6 +284,14 @@ def pa_decode_append(layout, out, q, k_cache, v_cache, key, value, slot_mapping,
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
         _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"),
         _stream()), "pa_decode_append")
+
+
+def pa_measure_read_stream(src, sink, work_groups: int = 0) -> None:
+    """One streaming read of the whole of `src` (device tensor) on the
+    current stream; `sink`: a device tensor with at least one int32."""
+    _check(lib().pa_measure_read_stream(_dev(src, "src"), src.numel() * src.element_size(),
+                                        _dev(sink, "sink"), int(work_groups), _stream()),
+           "pa_measure_read_stream")
 
 
 def pa_decode_shared_prefix(layout, out, q, k_cache, v_cache, block_table, seq_lens,

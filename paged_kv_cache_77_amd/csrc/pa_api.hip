@@ -517,6 +517,14 @@ int pa_debug_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n, void* st
   return hip_status(pa::launch_fp8_to_f16(codes, out, n, (hipStream_t)stream));
 }
 
+int pa_measure_read_stream(const void* src, size_t bytes, uint32_t* sink, int32_t work_groups,
+                           void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink || !aligned16(src) || bytes % 16 != 0) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_read_stream(src, (int64_t)bytes, sink, work_groups,
+                                           (hipStream_t)stream));
+}
+
 int pa_validate_metadata(const int32_t* block_table, int32_t bt_stride,
                          const int32_t* query_start_loc, const int32_t* seq_lens,
                          int32_t num_reqs, const int64_t* slot_mapping, int32_t num_tokens,

@@ -294,4 +294,50 @@ hipError_t launch_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Measurement support: one streaming read of a buffer (16-byte non-temporal
+// loads, eight in flight per thread, grid-stride), the on-device read rate
+// the attention kernels' HBM rates are compared with.  Nothing is written
+// unless the XOR of a thread's data is 0xffffffff, which keeps the loads
+// from being removed.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t xor4(const u32x4_t v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t* __restrict__ src,
+                                                          int64_t n, uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  constexpr int U = 8;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= xor4(v[u]);
+  }
+  for (; i < n; i += stride) acc ^= xor4(__builtin_nontemporal_load(src + i));
+  if (acc == 0xffffffffu) sink[0] = acc;
+}
+
+hipError_t launch_read_stream(const void* src, int64_t bytes, uint32_t* sink, int32_t work_groups,
+                              hipStream_t st) {
+  const int64_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  int64_t per = work_groups;
+  if (per <= 0) {                       // default: eight 4-wave work-groups per compute unit
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    per = (int64_t)(cus > 0 ? cus : 1) * 8;
+  }
+  const int64_t groups = per < (n + 255) / 256 ? per : (n + 255) / 256;
+  hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)groups), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4_t*>(src), n, sink);
+  return hipGetLastError();
+}
+
 }  // namespace pa

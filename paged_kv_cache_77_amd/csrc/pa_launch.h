@@ -79,6 +79,10 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache,
 
 hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int32_t n,
                              hipStream_t stream);
+// One streaming read of `bytes` at src (measurement support).
+hipError_t launch_read_stream(const void* src, int64_t bytes, uint32_t* sink, int32_t work_groups,
+                              hipStream_t stream);
+
 hipError_t launch_fp8_to_f16(const uint8_t* codes, uint16_t* out, int32_t n,
                              hipStream_t stream);
 

@@ -118,6 +118,18 @@ def test_shared_prefix_rejects_bad_arguments_without_launch():
                                      None, None) == 0     # no requests: nothing to do
 
 
+def test_measure_read_stream_rejects_bad_arguments_without_launch():
+    """pa_measure_read_stream: 16-byte aligned source, whole 16-byte chunks,
+    a sink; zero bytes is a no-op."""
+    L = pa.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.pa_measure_read_stream(p, 100, p, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_measure_read_stream(ctypes.c_void_p(4100), 64, p, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_measure_read_stream(None, 64, p, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_measure_read_stream(p, 64, None, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_measure_read_stream(None, 0, None, 0, None) == 0
+
+
 def test_fp8_writes_need_scales():
     L = pa.lib()
     lay = pa.make_layout(10, 2, 128, 1)

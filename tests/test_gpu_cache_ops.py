@@ -191,3 +191,24 @@ def test_fp8_write_config4_scaled_bit_exact():
                                       cache_dtype="fp8", k_scale=w.k_scale, v_scale=w.v_scale)
     assert np.array_equal(d.k_cache.cpu().numpy(), kp)
     assert np.array_equal(d.v_cache.cpu().numpy(), vp)
+
+
+@pytest.mark.parametrize("pos", ["first", "middle", "last"])
+def test_measure_read_stream_reads_every_chunk(pos):
+    """pa_measure_read_stream: a zero buffer leaves the sink alone; a single
+    0xffffffff word anywhere (first chunk, inside the unrolled part, the
+    last chunk of the tail loop) makes its thread's XOR 0xffffffff and the
+    sink gets it -- every 16-byte chunk is read."""
+    import paged_kv_cache_77_amd as pa
+    print(f"\n[case] read stream, marker {pos}", flush=True)
+    n = (64 << 20) + 48                      # not a multiple of the grid stride
+    buf = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.pa_measure_read_stream(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == 0
+    idx = {"first": 0, "middle": (n // 4) // 2 + 5, "last": n // 4 - 1}[pos]
+    buf[idx] = -1
+    pa.pa_measure_read_stream(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == -1
