@@ -481,7 +481,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
               "no multi-GPU path.", file=sys.stderr)
         return 2
 

@@ -81,7 +81,7 @@ RUNS = {
 BENCH = "python3 bench.py --no-cpu-baseline --no-other-workloads"
 
 
-def commands(outdir: str = "gpurun_out/prof") -> list:
+def commands(outdir: str = "rocprof_out") -> list:
     """The rocprofv3 command lines (run from the repository root)."""
     cmds = []
     for name, r in RUNS.items():
@@ -162,7 +162,7 @@ def _calibration(outdir: str) -> tuple:
     return gib / (fk * 1024.0), gib / (wk * 1024.0), fk, wk
 
 
-def summarize(outdir: str = "gpurun_out/prof", profiles: str = "profiles") -> dict:
+def summarize(outdir: str = "rocprof_out", profiles: str = "profiles") -> dict:
     sys.path.insert(0, ROOT)
     from bench import kernel_source_sha       # the hash bench.py checks
     sha = kernel_source_sha()
