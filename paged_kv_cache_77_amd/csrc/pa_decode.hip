@@ -429,6 +429,75 @@ __global__ __launch_bounds__(256) void merge_few_kernel(
   for (int e = 0; e < E; ++e) out[unit * D + lane * E + e] = f32_to_bf16(acc[e] * inv);
 }
 
+// The same merge for 17..64 partitions: one wave per (request, query head),
+// four per work-group, everything in flight at once.  Lane q holds partition
+// q's weight l_q e^(m_q - m); every partition row is read up front, D/4
+// lanes per row with 16-byte loads (64 / (D/4) rows per load instruction);
+// each lane sums its rows with their weights (shuffled from the owning
+// lanes), and the row groups are combined across lanes at the end.
+constexpr int kMergeWaveParts = 64;
+#ifndef PA_MERGE_WAVE
+#define PA_MERGE_WAVE 1
+#endif
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_wave_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ tmp_out,
+    const float* __restrict__ max_logits, const float* __restrict__ exp_sums,
+    const int32_t* __restrict__ seq_lens, int32_t num_reqs, int32_t num_q_heads,
+    int32_t partition_size, int32_t max_num_partitions, int32_t max_used) {
+  constexpr int LPR = D / 4;                     // lanes per partition row
+  constexpr int RPL = kWave / LPR;               // rows per load instruction
+  constexpr int NL = kMergeWaveParts / RPL;      // load instructions per lane
+  const int lane = threadIdx.x % kWave;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;     // r * Hq + h
+  if (unit >= (int64_t)num_reqs * num_q_heads) return;
+  const int r = (int)(unit / num_q_heads);
+  int n = (seq_lens[r] + partition_size - 1) / partition_size;
+  if (max_used > 0) n = min(n, max_used);        // the last record may be an open tail
+  n = min(n, min(max_num_partitions, kMergeWaveParts));
+  const int64_t base = unit * max_num_partitions;
+  const int c = lane % LPR, grp = lane / LPR;
+  f32x4_t v[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int p = i * RPL + grp;
+    v[i] = p < n ? *reinterpret_cast<const f32x4_t*>(tmp_out + (base + p) * D + 4 * c)
+                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float m = lane < n ? max_logits[base + lane] : -INFINITY;
+  float M = m;
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) M = fmaxf(M, xor_lanes(M, s));
+  const float wgt = (lane < n && m != -INFINITY) ? exp_sums[base + lane] * fast_exp2((m - M) * kLog2e)
+                                                 : 0.f;
+  float L = wgt;
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) L += xor_lanes(L, s);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const float wp = __shfl(wgt, i * RPL + grp, kWave);
+    acc.x = fmaf(wp, v[i].x, acc.x);
+    acc.y = fmaf(wp, v[i].y, acc.y);
+    acc.z = fmaf(wp, v[i].z, acc.z);
+    acc.w = fmaf(wp, v[i].w, acc.w);
+  }
+#pragma unroll
+  for (int s = LPR; s < kWave; s <<= 1) {
+    acc.x += xor_lanes(acc.x, s);
+    acc.y += xor_lanes(acc.y, s);
+    acc.z += xor_lanes(acc.z, s);
+    acc.w += xor_lanes(acc.w, s);
+  }
+  if (lane < LPR) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const uint32_t w0 = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(out + unit * D + 4 * c) = make_uint2(w0, w1);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 
@@ -614,6 +683,19 @@ hipError_t launch_merge(void* out, const float* tmp_out, const float* max_logits
                          max_num_partitions, max_used);
     else
       hipLaunchKernelGGL(merge_few_kernel<128>, g4, dim3(256), 0, st, (uint16_t*)out, tmp_out,
+                         max_logits, exp_sums, seq_lens, num_reqs, num_q_heads, partition_size,
+                         max_num_partitions, max_used);
+    return hipGetLastError();
+  }
+  if (PA_MERGE_WAVE && parts <= kMergeWaveParts) {
+    const int64_t units = (int64_t)num_reqs * num_q_heads;
+    const dim3 g4((unsigned)((units + 3) / 4));
+    if (head_dim == 64)
+      hipLaunchKernelGGL(merge_wave_kernel<64>, g4, dim3(256), 0, st, (uint16_t*)out, tmp_out,
+                         max_logits, exp_sums, seq_lens, num_reqs, num_q_heads, partition_size,
+                         max_num_partitions, max_used);
+    else
+      hipLaunchKernelGGL(merge_wave_kernel<128>, g4, dim3(256), 0, st, (uint16_t*)out, tmp_out,
                          max_logits, exp_sums, seq_lens, num_reqs, num_q_heads, partition_size,
                          max_num_partitions, max_used);
     return hipGetLastError();

@@ -7,7 +7,7 @@ import oracle
 from paged_kv_cache_77_amd import workloads as wl
 from paged_kv_cache_77_amd import device as dv
 import paged_kv_cache_77_amd as pa
-from tests.parity import check_bf16
+from tests.parity import check_bf16, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -519,3 +519,42 @@ def test_partition_ranges_merge_like_one_call():
     assert torch.equal(tmp2, tmp) and torch.equal(ml2, ml) and torch.equal(es2, es)
     assert np.array_equal(dv.bits_of(out), dv.bits_of(full))
     check_bf16(dv.bits_of(out), oracle.decode(w), "range merge")
+
+
+@pytest.mark.parametrize("pmax,d", [(16, 128), (64, 128), (64, 64), (40, 128), (100, 128)])
+def test_merge_partitions_on_synthetic_partials(pmax, d):
+    """pa_merge_partitions on random partials (m in natural-log units over a
+    wide range, l > 0, O ~ N(0,1)) against the oracle's merge of the same
+    fp32 values, with per-request partition counts from 0 to pmax; entries
+    past each request's count are NaN and must not be read.  pmax 16, up to
+    64 and over 64 take the three merge kernels."""
+    _announce(f"merge on synthetic partials pmax={pmax} d={d}")
+    P = 16
+    rng = np.random.default_rng(70 + pmax + d)
+    counts = np.array([0, 1, pmax, pmax - 1, max(1, pmax // 2), 17 if pmax > 17 else 2, 3])
+    R, H = len(counts), 8
+    seq_lens = (counts * P - rng.integers(0, P, size=R) * (counts > 0)).astype(np.int32)
+    assert np.array_equal((seq_lens + P - 1) // P, counts)
+    m = rng.uniform(-30, 30, size=(R, H, pmax)).astype(np.float32)
+    l = rng.uniform(0.5, 200, size=(R, H, pmax)).astype(np.float32)
+    O = rng.standard_normal((R, H, pmax, d)).astype(np.float32)
+    for r, n in enumerate(counts):
+        m[r, :, n:] = np.nan
+        l[r, :, n:] = np.nan
+        O[r, :, n:] = np.nan
+    out = torch.full((R, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pa.pa_merge_partitions(out, torch.from_numpy(O).cuda(), torch.from_numpy(m).cuda(),
+                           torch.from_numpy(l).cuda(), torch.from_numpy(seq_lens).cuda(), P)
+    torch.cuda.synchronize()
+    got = dv.bits_of(out)
+    ref = oracle.merge_partitions(m.astype(np.float64), l.astype(np.float64),
+                                  O.astype(np.float64), counts)
+    assert np.all(got[0] == 0)                       # no partition: zero row
+    # outputs here are O(1) (one partition usually dominates), so bf16
+    # rounding alone is ~1e-3 on average: the check is per element, within
+    # one bf16 ulp of the fp64 merge (correct up to the final rounding)
+    g, r = oracle.bf16_bits_to_f64(got[1:]), ref[1:]
+    assert np.all(np.isfinite(g))
+    err = np.abs(g - r)
+    # (plus 1e-6 absolute: fp32 sums of O(1) terms near a cancelling zero)
+    assert np.all(err <= np.maximum(ulp_bf16(r), 1e-6)), f"merge pmax={pmax}: max err {err.max():.3g}"
