@@ -199,3 +199,40 @@ def test_hash_without_parent_is_caught(monkeypatch):
     monkeypatch.setattr(bpm, "block_hash", lambda parent, tokens, extra=0:
                         real(bpm.NONE_HASH, tokens, extra))
     _fails(_pins_blocks().test_block_hash_chain_property)
+
+
+def test_fp8_dequant_dividing_by_the_scale_is_caught(monkeypatch):
+    def wrong(pool, cache_dtype, scale=1.0):
+        if cache_dtype == "fp8":
+            return po.fp8_e4m3fn_to_f64(pool) / np.float64(np.float32(scale))
+        return po.bf16_bits_to_f64(pool)
+    monkeypatch.setattr(po, "cache_values", wrong)
+    _fails(pins.test_fp8_dequant_multiplies_by_its_scale)
+    _fails(pins.test_decode_fp8_each_scale_applies_to_its_tensor)
+    _fails(pins.test_prefill_fp8_each_scale_applies_to_its_tensor)
+
+
+def test_fp8_write_of_v_with_k_scale_is_caught(monkeypatch):
+    real = po.reshape_and_cache
+
+    def wrong(k_pool, v_pool, key, value, slots, block_size, cache_dtype="bf16",
+              k_scale=1.0, v_scale=1.0):
+        return real(k_pool, v_pool, key, value, slots, block_size, cache_dtype,
+                    k_scale, k_scale)
+    monkeypatch.setattr(po, "reshape_and_cache", wrong)
+    _fails(pins.test_fp8_scatter_writes_codes_of_the_quotient)
+
+
+def test_fp8_read_of_v_with_k_scale_is_caught(monkeypatch):
+    def wrong(w, r, k_pool=None, v_pool=None):
+        kp = w.k_pool if k_pool is None else k_pool
+        vp = w.v_pool if v_pool is None else v_pool
+        n = int(w.seq_lens[r])
+        K = po.cache_values(po.gather_kv(kp, w.block_table[r], n, w.block_size),
+                            w.cache_dtype, w.k_scale)
+        V = po.cache_values(po.gather_kv(vp, w.block_table[r], n, w.block_size),
+                            w.cache_dtype, w.k_scale)
+        return K, V
+    monkeypatch.setattr(po, "_request_kv", wrong)
+    _fails(pins.test_decode_fp8_each_scale_applies_to_its_tensor)
+    _fails(pins.test_prefill_fp8_each_scale_applies_to_its_tensor)

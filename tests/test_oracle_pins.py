@@ -428,6 +428,81 @@ def test_fp8_encode_ties_saturation_and_specials():
     assert e(-0.0) == 0x80 and e(0.0) == 0x00 and e(-1e-9) == 0x80
 
 
+def _torch_dequant(codes, scale):
+    """FP8 codes -> fp64 through torch's float8_e4m3fn type, times the
+    per-tensor scale (the read side: the code's value times its scale)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy() * float(np.float32(scale))
+
+
+def _torch_quant(x, scale):
+    """fp32 values -> E4M3FN codes of x / scale by torch's cast."""
+    y = np.ascontiguousarray(x, dtype=np.float32) / np.float32(scale)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_dequant_multiplies_by_its_scale():
+    """An FP8 cache element is its code's value times the tensor's scale ("vLLM
+    深度解析（二）" §3.2.1/§3.2.4: quantised K/V vectors are converted with the
+    scale, scaled_convert(..., *k_scale)).  Values quantised by torch's cast
+    of x / s come back within half a code step of x, and equal torch's own
+    decode times s."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(4096) * 3).astype(np.float32)
+    amax = float(np.abs(x).max())
+    for s in (amax / 448, amax / 100, amax / 448 * 7, 0.5, 3.0):
+        s = np.float32(max(s, amax / 448))
+        codes = _torch_quant(x, s)
+        back = oracle.cache_values(codes, "fp8", s)
+        # half a code step: 2^-4 relative for normals, 2^-10 * s for subnormals
+        assert np.all(np.abs(back - x) <= np.abs(x) / 16 + 2.0 ** -10 * float(s)), float(s)
+        assert np.array_equal(back, _torch_dequant(codes, s)), float(s)
+
+
+def _contiguous_codes(w, r, which):
+    """Raw cache elements of request r's logical K or V in a workload built
+    with the identity permutation (block range reshaped, no table)."""
+    pool = w.k_pool if which == "k" else w.v_pool
+    nblk = [(-(-int(s) // 16)) for s in w.seq_lens]
+    start = sum(nblk[:r])
+    blk = pool[start:start + nblk[r]]
+    x = blk.transpose(0, 2, 1, 3).reshape(-1, w.num_kv_heads, w.head_dim)
+    return x[: int(w.seq_lens[r])]
+
+
+def test_decode_fp8_each_scale_applies_to_its_tensor():
+    """K is dequantised with k_scale and V with v_scale, by multiplication:
+    the reference decodes the codes with torch and runs torch's fp64 SDPA.
+    The scales differ from each other and from 1 by large factors, so a swap
+    or a division moves the output far outside 1e-12."""
+    w = wl.make_workload(name="t", seq_lens=[3, 33, 64], q_lens=[1] * 3,
+                         num_q_heads=8, num_kv_heads=2, head_dim=64, seed=22,
+                         cache_dtype="fp8", writes_new_kv=False, identity_perm=True)
+    w.k_scale, w.v_scale = np.float32(0.0213), np.float32(0.37)
+    out = oracle.decode(w)
+    for r in range(w.num_reqs):
+        K = _torch_dequant(_contiguous_codes(w, r, "k"), w.k_scale)
+        V = _torch_dequant(_contiguous_codes(w, r, "v"), w.v_scale)
+        q = oracle.bf16_bits_to_f64(w.q[r])[None]
+        np.testing.assert_allclose(out[r], sdpa64(q, K, V, w.scale)[0], rtol=0, atol=1e-12)
+
+
+def test_prefill_fp8_each_scale_applies_to_its_tensor():
+    """The same for a causal prefill over an FP8 cache (torch's causal SDPA)."""
+    w = wl.make_workload(name="t", seq_lens=[40, 17], q_lens=[40, 17], num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, seed=23, cache_dtype="fp8",
+                         writes_new_kv=False, identity_perm=True)
+    w.k_scale, w.v_scale = np.float32(2.5), np.float32(0.0177)
+    out = oracle.prefill_varlen(w)
+    for r in range(w.num_reqs):
+        K = _torch_dequant(_contiguous_codes(w, r, "k"), w.k_scale)
+        V = _torch_dequant(_contiguous_codes(w, r, "v"), w.v_scale)
+        lo, hi = w.query_start_loc[r], w.query_start_loc[r + 1]
+        q = oracle.bf16_bits_to_f64(w.q[lo:hi])
+        np.testing.assert_allclose(out[lo:hi], sdpa64(q, K, V, w.scale, causal=True),
+                                   rtol=0, atol=1e-12)
+
+
 def test_fp8_scatter_writes_codes_of_the_quotient():
     w = wl.make_workload(name="t", seq_lens=[3, 20], q_lens=[1, 2], num_q_heads=4,
                          num_kv_heads=2, head_dim=64, seed=5, cache_dtype="fp8")
@@ -446,6 +521,18 @@ def test_fp8_scatter_writes_codes_of_the_quotient():
     untouched = np.ones(kp.shape[0], bool)
     untouched[sm // 16] = False
     assert np.array_equal(kp[untouched], w.k_pool[untouched])
+    # each pool takes its own scale: K with k_scale, V with v_scale (scales
+    # far apart), against torch's cast of the quotient
+    ks, vs = np.float32(0.0419), np.float32(0.00731)
+    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, sm, 16,
+                                      cache_dtype="fp8", k_scale=ks, v_scale=vs)
+    for j, s in enumerate(sm):
+        blk, off = s // 16, s % 16
+        xk = oracle.bf16_bits_to_f64(w.k_new[j]).astype(np.float32)
+        xv = oracle.bf16_bits_to_f64(w.v_new[j]).astype(np.float32)
+        assert np.array_equal(kp[blk, :, off, :], _torch_quant(xk, ks))
+        assert np.array_equal(vp[blk, :, off, :], _torch_quant(xv, vs))
+    assert np.array_equal(vp[untouched], w.v_pool[untouched])
 
 
 # ---------------------------------------------------------------------------
