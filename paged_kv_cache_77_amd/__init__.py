@@ -155,6 +155,90 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# ---------------------------------------------------------------------------
+# Argument checks made before any launch.  The kernels trust dtypes and
+# sizes (a pool smaller than its layout, or an int64 table read as int32,
+# would be read or written out of bounds on the device), so the binding
+# rejects mismatches with ValueError first.  Checks that need no device
+# (dtype, rank, sizes) come before the device check, so they hold on a host
+# without a GPU too.
+
+def _need(t, name: str, dtype, dims=None, min_numel: int = 0, optional: bool = False):
+    """t must have `dtype`; `dims` (a tuple, None entries free) fixes its
+    rank and sizes; at least `min_numel` elements."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if dims is not None:
+        if t.dim() != len(dims):
+            raise ValueError(f"{name}: {t.dim()} dimensions, expected {len(dims)}")
+        for i, want in enumerate(dims):
+            if want is not None and t.shape[i] != want:
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, dimension {i} must be {want}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+
+
+def _cache_elem_dtype(layout) -> torch.dtype:
+    return torch.uint8 if layout.cache_dtype == PA_CACHE_FP8_E4M3 else torch.bfloat16
+
+
+def _need_pools(layout, k_cache, v_cache) -> None:
+    """K and V pools: the layout's element type and at least num_blocks
+    (num_kv_heads, block_size, head_dim) tiles each."""
+    n = (int(layout.num_blocks) * int(layout.num_kv_heads) * int(layout.block_size) *
+         int(layout.head_dim))
+    dt = _cache_elem_dtype(layout)
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, dt, min_numel=n)
+        if t.dim() == 4 and (tuple(t.shape[1:]) != (layout.num_kv_heads, layout.block_size,
+                                                     layout.head_dim)
+                             or t.shape[0] < layout.num_blocks):
+            raise ValueError(f"{name}: shape {tuple(t.shape)} does not hold the layout's "
+                             f"[{layout.num_blocks}][{layout.num_kv_heads}]"
+                             f"[{layout.block_size}][{layout.head_dim}] tiles")
+
+
+def _need_scales(layout, k_scale, v_scale) -> None:
+    fp8 = layout.cache_dtype == PA_CACHE_FP8_E4M3
+    _need(k_scale, "k_scale", torch.float32, min_numel=1, optional=not fp8)
+    _need(v_scale, "v_scale", torch.float32, min_numel=1, optional=not fp8)
+
+
+def _need_rows(layout, q, out, rows, num_q_heads, what="q") -> None:
+    """q and out: bf16 [rows][num_q_heads][head_dim]."""
+    dims = (rows, num_q_heads, int(layout.head_dim))
+    _need(q, what, torch.bfloat16, dims)
+    if out is not None:
+        _need(out, "out", torch.bfloat16, dims)
+
+
+def _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes) -> None:
+    _need(q, "q", torch.bfloat16, (None, None, int(layout.head_dim)))
+    R, H = int(q.shape[0]), int(q.shape[1])
+    _need_rows(layout, q, out, R, H)
+    _need_pools(layout, k_cache, v_cache)
+    _need(block_table, "block_table", torch.int32, (None, None))
+    if block_table.shape[0] < R:
+        raise ValueError(f"block_table: {block_table.shape[0]} rows for {R} requests")
+    _need(seq_lens, "seq_lens", torch.int32, (R,))
+    _need_scales(layout, k_scale, v_scale)
+    _need(alibi_slopes, "alibi_slopes", torch.float32, (H,), optional=True)
+
+
+def _need_partials(tmp_out, max_logits, exp_sums, R, H, D) -> None:
+    _need(max_logits, "max_logits", torch.float32, (R, H, None))
+    P = int(max_logits.shape[2])
+    _need(exp_sums, "exp_sums", torch.float32, (R, H, P))
+    _need(tmp_out, "tmp_out", torch.float32, (R, H, P, D))
+
+
 def pa_kv_cache_bytes(layout: PaKvLayout) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().pa_kv_cache_bytes(ctypes.byref(layout), ctypes.byref(n)), "pa_kv_cache_bytes")
@@ -163,6 +247,13 @@ def pa_kv_cache_bytes(layout: PaKvLayout) -> int:
 
 def pa_compute_slot_mapping(slot_mapping, block_table, query_start_loc, seq_lens,
                             block_size: int = 16) -> None:
+    _need(seq_lens, "seq_lens", torch.int32, (None,))
+    R = int(seq_lens.shape[0])
+    _need(query_start_loc, "query_start_loc", torch.int32, (R + 1,))
+    _need(block_table, "block_table", torch.int32, (None, None))
+    if block_table.shape[0] < R:
+        raise ValueError(f"block_table: {block_table.shape[0]} rows for {R} requests")
+    _need(slot_mapping, "slot_mapping", torch.int64, (None,))
     _check(lib().pa_compute_slot_mapping(
         _dev(slot_mapping, "slot_mapping"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(query_start_loc, "query_start_loc"),
@@ -172,6 +263,12 @@ def pa_compute_slot_mapping(slot_mapping, block_table, query_start_loc, seq_lens
 
 def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping, k_scale=None,
                          v_scale=None) -> None:
+    kv = (None, int(layout.num_kv_heads), int(layout.head_dim))
+    _need(key, "key", torch.bfloat16, kv)
+    _need(value, "value", torch.bfloat16, (key.shape[0],) + kv[1:])
+    _need_pools(layout, k_cache, v_cache)
+    _need(slot_mapping, "slot_mapping", torch.int64, (None,), min_numel=int(key.shape[0]))
+    _need_scales(layout, k_scale, v_scale)
     _check(lib().pa_reshape_and_cache(
         ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(key, "key"), _dev(value, "value"), key.shape[0],
@@ -182,6 +279,19 @@ def pa_reshape_and_cache(layout, k_cache, v_cache, key, value, slot_mapping, k_s
 def pa_reshape_and_cache_varlen(layout, k_cache, v_cache, key, value, block_table,
                                 query_start_loc, seq_lens, slot_mapping=None, k_scale=None,
                                 v_scale=None) -> None:
+    kv = (None, int(layout.num_kv_heads), int(layout.head_dim))
+    _need(key, "key", torch.bfloat16, kv)
+    T = int(key.shape[0])
+    _need(value, "value", torch.bfloat16, (T,) + kv[1:])
+    _need_pools(layout, k_cache, v_cache)
+    _need(seq_lens, "seq_lens", torch.int32, (None,))
+    R = int(seq_lens.shape[0])
+    _need(query_start_loc, "query_start_loc", torch.int32, (R + 1,))
+    _need(block_table, "block_table", torch.int32, (None, None))
+    if block_table.shape[0] < R:
+        raise ValueError(f"block_table: {block_table.shape[0]} rows for {R} requests")
+    _need(slot_mapping, "slot_mapping", torch.int64, (None,), min_numel=T, optional=True)
+    _need_scales(layout, k_scale, v_scale)
     _check(lib().pa_reshape_and_cache_varlen(
         ctypes.byref(layout), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(key, "key"), _dev(value, "value"), _dev(block_table, "block_table"),
@@ -193,6 +303,9 @@ def pa_reshape_and_cache_varlen(layout, k_cache, v_cache, key, value, block_tabl
 
 def pa_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
               scale: float, k_scale=None, v_scale=None, alibi_slopes=None) -> None:
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
     _check(lib().pa_decode(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
@@ -211,6 +324,10 @@ def pa_decode_plan_for(layout, num_reqs: int, num_q_heads: int, max_seq_len: int
 def pa_decode_auto(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
                    scale: float, plan: PaDecodePlan, workspace=None, k_scale=None,
                    v_scale=None, alibi_slopes=None) -> None:
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _need(workspace, "workspace", torch.uint8, optional=True)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_decode_auto(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
@@ -228,6 +345,10 @@ def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:
 def pa_decode_balanced(layout, out, q, k_cache, v_cache, block_table, seq_lens,
                        max_seq_len: int, scale: float, workspace, k_scale=None,
                        v_scale=None, alibi_slopes=None) -> None:
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _need(workspace, "workspace", torch.uint8)
     _check(lib().pa_decode_balanced(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
@@ -241,6 +362,9 @@ def pa_decode_partitioned(layout, q, k_cache, v_cache, block_table, seq_lens,
                           max_seq_len: int, scale: float, partition_size: int, tmp_out,
                           max_logits, exp_sums, k_scale=None, v_scale=None,
                           alibi_slopes=None) -> None:
+    _need_decode(layout, None, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _need_partials(tmp_out, max_logits, exp_sums, q.shape[0], q.shape[1], layout.head_dim)
     _check(lib().pa_decode_partitioned(
         ctypes.byref(layout), _dev(q, "q"), q.shape[0], q.shape[1], _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_table, "block_table"), block_table.shape[1],
@@ -255,6 +379,9 @@ def pa_decode_partitioned_range(layout, q, k_cache, v_cache, block_table, seq_le
                                 max_seq_len: int, scale: float, partition_size: int,
                                 part_begin: int, part_end: int, tmp_out, max_logits, exp_sums,
                                 k_scale=None, v_scale=None, alibi_slopes=None) -> None:
+    _need_decode(layout, None, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _need_partials(tmp_out, max_logits, exp_sums, q.shape[0], q.shape[1], layout.head_dim)
     _check(lib().pa_decode_partitioned_range(
         ctypes.byref(layout), _dev(q, "q"), q.shape[0], q.shape[1], _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_table, "block_table"), block_table.shape[1],
@@ -267,6 +394,10 @@ def pa_decode_partitioned_range(layout, q, k_cache, v_cache, block_table, seq_le
 
 def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,
                         partition_size: int) -> None:
+    _need(out, "out", torch.bfloat16, (None, None, None))
+    R, H, D = (int(x) for x in out.shape)
+    _need(seq_lens, "seq_lens", torch.int32, (R,))
+    _need_partials(tmp_out, max_logits, exp_sums, R, H, D)
     _check(lib().pa_merge_partitions(
         _dev(out, "out"), _dev(tmp_out, "tmp_out"), _dev(max_logits, "max_logits"),
         _dev(exp_sums, "exp_sums"), _dev(seq_lens, "seq_lens"), seq_lens.shape[0],
@@ -277,6 +408,13 @@ def pa_merge_partitions(out, tmp_out, max_logits, exp_sums, seq_lens,
 def pa_decode_append(layout, out, q, k_cache, v_cache, key, value, slot_mapping, block_table,
                      seq_lens, max_seq_len: int, scale: float, k_scale=None, v_scale=None,
                      alibi_slopes=None) -> None:
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    kv = (int(q.shape[0]), int(layout.num_kv_heads), int(layout.head_dim))
+    _need(key, "key", torch.bfloat16, kv)
+    _need(value, "value", torch.bfloat16, kv)
+    _need(slot_mapping, "slot_mapping", torch.int64, (None,), min_numel=kv[0], optional=True)
     _check(lib().pa_decode_append(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(key, "key"),
@@ -298,6 +436,10 @@ def pa_decode_shared_prefix(layout, out, q, k_cache, v_cache, block_table, seq_l
                             max_seq_len: int, scale: float, shared_blocks: int,
                             partition_size: int, tmp_out, max_logits, exp_sums,
                             k_scale=None, v_scale=None, alibi_slopes=None) -> None:
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _need_partials(tmp_out, max_logits, exp_sums, q.shape[0], q.shape[1], layout.head_dim)
     _check(lib().pa_decode_shared_prefix(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
@@ -311,6 +453,19 @@ def pa_decode_shared_prefix(layout, out, q, k_cache, v_cache, block_table, seq_l
 def pa_prefill_varlen(layout, out, q, k_cache, v_cache, query_start_loc, seq_lens,
                       block_table, max_query_len: int, max_seq_len: int, scale: float,
                       k_scale=None, v_scale=None, alibi_slopes=None) -> None:
+    _need(q, "q", torch.bfloat16, (None, None, int(layout.head_dim)))
+    T, H = int(q.shape[0]), int(q.shape[1])
+    _need_rows(layout, q, out, T, H)
+    _need(out, "out", torch.bfloat16)
+    _need_pools(layout, k_cache, v_cache)
+    _need(seq_lens, "seq_lens", torch.int32, (None,))
+    R = int(seq_lens.shape[0])
+    _need(query_start_loc, "query_start_loc", torch.int32, (R + 1,))
+    _need(block_table, "block_table", torch.int32, (None, None))
+    if block_table.shape[0] < R:
+        raise ValueError(f"block_table: {block_table.shape[0]} rows for {R} requests")
+    _need_scales(layout, k_scale, v_scale)
+    _need(alibi_slopes, "alibi_slopes", torch.float32, (H,), optional=True)
     _check(lib().pa_prefill_varlen(
         ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -323,6 +478,16 @@ def pa_prefill_varlen(layout, out, q, k_cache, v_cache, query_start_loc, seq_len
 
 def pa_debug_gather_kv(layout, k_out, v_out, k_cache, v_cache, block_table, seq_lens,
                        cu_seq_lens, max_seq_len: int) -> None:
+    _need_pools(layout, k_cache, v_cache)
+    _need(seq_lens, "seq_lens", torch.int32, (None,))
+    R = int(seq_lens.shape[0])
+    _need(cu_seq_lens, "cu_seq_lens", torch.int32, (R + 1,))
+    _need(block_table, "block_table", torch.int32, (None, None))
+    if block_table.shape[0] < R:
+        raise ValueError(f"block_table: {block_table.shape[0]} rows for {R} requests")
+    dt = _cache_elem_dtype(layout)
+    _need(k_out, "k_out", dt, (None, int(layout.num_kv_heads), int(layout.head_dim)))
+    _need(v_out, "v_out", dt, tuple(k_out.shape))
     _check(lib().pa_debug_gather_kv(
         ctypes.byref(layout), _dev(k_out, "k_out"), _dev(v_out, "v_out"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
@@ -331,11 +496,17 @@ def pa_debug_gather_kv(layout, k_out, v_out, k_cache, v_cache, block_table, seq_
 
 
 def pa_debug_fp8_to_f32(codes, out) -> None:
+    _need(codes, "codes", torch.uint8)
+    _need(out, "out", torch.float32, min_numel=codes.numel())
     _check(lib().pa_debug_fp8_to_f32(_dev(codes, "codes"), _dev(out, "out"), codes.numel(),
                                      _stream()), "pa_debug_fp8_to_f32")
 
 
 def pa_debug_fp8_to_f16(codes, out) -> None:
+    _need(codes, "codes", torch.uint8)
+    if out is None or out.dtype not in (torch.int16, torch.float16, torch.uint16):
+        raise ValueError("out: a 16-bit tensor is required")
+    _need(out, "out", out.dtype, min_numel=codes.numel())
     _check(lib().pa_debug_fp8_to_f16(_dev(codes, "codes"), _dev(out, "out"), codes.numel(),
                                      _stream()), "pa_debug_fp8_to_f16")
 

@@ -228,3 +228,114 @@ def test_decode_auto_rejects_small_workspace():
                             None) == pa.PA_ERR_INVALID_ARG
     assert L.pa_decode_auto(ctypes.byref(lay), p, p, 1, 32, p, p, p, 512, p, 8192, 0.1, None,
                             None, None, None, p, 0, None) == pa.PA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# the Python binding's checks: wrong dtypes and undersized buffers are
+# rejected with ValueError before anything reaches the library (host
+# tensors here: every check below fires before the device check)
+
+def _host_decode_args(layout, R=4, H=8, D=64, NB=12, W=5):
+    import torch
+    dt = torch.uint8 if layout.cache_dtype == pa.PA_CACHE_FP8_E4M3 else torch.bfloat16
+    return dict(
+        out=torch.zeros((R, H, D), dtype=torch.bfloat16),
+        q=torch.zeros((R, H, D), dtype=torch.bfloat16),
+        k_cache=torch.zeros((NB, layout.num_kv_heads, 16, D), dtype=dt),
+        v_cache=torch.zeros((NB, layout.num_kv_heads, 16, D), dtype=dt),
+        block_table=torch.zeros((R, W), dtype=torch.int32),
+        seq_lens=torch.ones((R,), dtype=torch.int32),
+        max_seq_len=16, scale=0.125)
+
+
+def _rejects(fn, match, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(**kw)
+
+
+def test_binding_accepts_consistent_host_args_up_to_the_device_check():
+    lay = pa.make_layout(12, 2, 64, 0)
+    _rejects(pa.pa_decode, "GPU tensor", layout=lay, **_host_decode_args(lay))
+
+
+@pytest.mark.parametrize("name,bad,match", [
+    ("seq_lens", ("int64", None), "seq_lens: dtype"),
+    ("block_table", ("int64", None), "block_table: dtype"),
+    ("q", ("float32", None), "q: dtype"),
+    ("out", ("float16", None), "out: dtype"),
+    ("k_cache", ("uint8", None), "k_cache: dtype"),
+    ("v_cache", (None, (11, 2, 16, 64)), "v_cache"),          # one block short
+    ("k_cache", (None, (12, 2, 8, 64)), "k_cache"),           # wrong tile shape
+    ("out", (None, (4, 8, 128)), "out: shape"),
+    ("seq_lens", (None, (3,)), "seq_lens: shape"),
+    ("block_table", (None, (3, 5)), "block_table: 3 rows"),
+])
+def test_binding_rejects_bad_decode_args(name, bad, match):
+    import torch
+    lay = pa.make_layout(12, 2, 64, 0)
+    args = _host_decode_args(lay)
+    dtype, shape = bad
+    t = args[name]
+    args[name] = torch.zeros(shape if shape is not None else tuple(t.shape),
+                             dtype=getattr(torch, dtype) if dtype else t.dtype)
+    _rejects(pa.pa_decode, match, layout=lay, **args)
+
+
+def test_binding_rejects_bad_fp8_scales_and_slopes():
+    import torch
+    lay = pa.make_layout(12, 2, 64, pa.PA_CACHE_FP8_E4M3)
+    args = _host_decode_args(lay)
+    _rejects(pa.pa_decode, "k_scale is required", layout=lay, **args)
+    _rejects(pa.pa_decode, "k_scale: dtype", layout=lay,
+             k_scale=torch.ones(1, dtype=torch.float64), v_scale=torch.ones(1), **args)
+    _rejects(pa.pa_decode, "alibi_slopes: shape", layout=lay, k_scale=torch.ones(1),
+             v_scale=torch.ones(1), alibi_slopes=torch.ones(4), **args)
+    # bf16 pools in an FP8 layout
+    args["k_cache"] = torch.zeros((12, 2, 16, 64), dtype=torch.bfloat16)
+    _rejects(pa.pa_decode, "k_cache: dtype", layout=lay, k_scale=torch.ones(1),
+             v_scale=torch.ones(1), **args)
+
+
+def test_binding_rejects_bad_write_and_prefill_args():
+    import torch
+    lay = pa.make_layout(12, 2, 64, 0)
+    kc = torch.zeros((12, 2, 16, 64), dtype=torch.bfloat16)
+    key = torch.zeros((5, 2, 64), dtype=torch.bfloat16)
+    sm32 = torch.zeros((5,), dtype=torch.int32)
+    _rejects(pa.pa_reshape_and_cache, "slot_mapping: dtype", layout=lay, k_cache=kc,
+             v_cache=kc, key=key, value=key, slot_mapping=sm32)
+    _rejects(pa.pa_reshape_and_cache, "slot_mapping: 4 elements", layout=lay, k_cache=kc,
+             v_cache=kc, key=key, value=key, slot_mapping=torch.zeros(4, dtype=torch.int64))
+    _rejects(pa.pa_reshape_and_cache, "value: shape", layout=lay, k_cache=kc, v_cache=kc,
+             key=key, value=torch.zeros((5, 1, 64), dtype=torch.bfloat16),
+             slot_mapping=torch.zeros(5, dtype=torch.int64))
+    q = torch.zeros((7, 4, 64), dtype=torch.bfloat16)
+    kw = dict(layout=lay, out=torch.zeros((7, 4, 64), dtype=torch.bfloat16), q=q, k_cache=kc,
+              v_cache=kc, query_start_loc=torch.tensor([0, 2, 7], dtype=torch.int32),
+              seq_lens=torch.tensor([4, 9], dtype=torch.int32),
+              block_table=torch.zeros((2, 3), dtype=torch.int32), max_query_len=5,
+              max_seq_len=9, scale=0.125)
+    _rejects(pa.pa_prefill_varlen, "GPU tensor", **kw)
+    bad = dict(kw, query_start_loc=torch.tensor([0, 2, 7], dtype=torch.int64))
+    _rejects(pa.pa_prefill_varlen, "query_start_loc: dtype", **bad)
+    bad = dict(kw, query_start_loc=torch.tensor([0, 7], dtype=torch.int32))
+    _rejects(pa.pa_prefill_varlen, "query_start_loc: shape", **bad)
+    bad = dict(kw, out=torch.zeros((6, 4, 64), dtype=torch.bfloat16))
+    _rejects(pa.pa_prefill_varlen, "out: shape", **bad)
+
+
+def test_binding_rejects_mismatched_partials():
+    import torch
+    lay = pa.make_layout(12, 2, 64, 0)
+    args = _host_decode_args(lay)
+    del args["out"]
+    R, H, D = 4, 8, 64
+    tmp = torch.zeros((R, H, 3, D))
+    ml = torch.zeros((R, H, 3))
+    es = torch.zeros((R, H, 2))
+    _rejects(pa.pa_decode_partitioned, "exp_sums: shape", layout=lay, partition_size=16,
+             tmp_out=tmp, max_logits=ml, exp_sums=es, **args)
+    _rejects(pa.pa_merge_partitions, "tmp_out: dtype",
+             out=torch.zeros((R, H, D), dtype=torch.bfloat16), tmp_out=tmp.double(),
+             max_logits=ml, exp_sums=torch.zeros((R, H, 3)),
+             seq_lens=torch.ones(R, dtype=torch.int32), partition_size=16)
