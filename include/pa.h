@@ -12,7 +12,8 @@
  * ---------------------------------------
  *  - Every pointer argument except `layout`, `bytes_per_pool` and the host
  *    arrays of pa_validate_metadata is a DEVICE pointer owned by the caller;
- *    the library never allocates, frees or retains memory and keeps no state.
+ *    the library never allocates, frees or retains memory, and keeps no state
+ *    besides pa_decode_auto_static's static scratch array (one per device).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises the stream.
  *  - Return value: PA_OK (0) on success, a negative pa_status otherwise.
@@ -53,6 +54,8 @@ enum pa_status {
   PA_ERR_UNSUPPORTED = -2,  /* head_dim, block_size, dtype or head ratio not built */
   PA_ERR_HIP = -3,          /* a HIP launch failed */
   PA_ERR_METADATA = -4,     /* pa_validate_metadata found an inconsistency */
+  PA_ERR_SCRATCH = -5,      /* pa_decode_auto_static: the plan needs more than
+                               PA_STATIC_SCRATCH_BYTES of scratch */
 };
 
 enum pa_cache_dtype {
@@ -330,6 +333,35 @@ int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t
                    const float* v_scale, const float* alibi_slopes,
                    const pa_decode_plan* plan, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * pa_decode_auto without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split path's partials (tmp_out,
+ * max_logits, exp_sums, laid out as pa_decode_auto carves them) live in a
+ * static device array of PA_STATIC_SCRATCH_BYTES inside the library, one
+ * per device, held until the process ends; the call allocates nothing.
+ * Its device address is looked up on the first call made with a device
+ * current.  The result equals pa_decode_auto's.
+ *  - A split plan whose workspace_bytes would exceed PA_STATIC_SCRATCH_BYTES
+ *    returns PA_ERR_SCRATCH and launches nothing (32 MiB hold, e.g., 8
+ *    requests x 32 query heads x 64 partitions of head_dim 128 with room to
+ *    spare); single-pass plans need no scratch.
+ *  - Every call on one device shares that device's array: calls that
+ *    overlap in time on one device (two streams, or two host threads) race.
+ *    Calls in order on one stream are safe.  Nothing in the array needs to
+ *    start at zero (every partial a merge reads is written first).
+ * Arguments as pa_decode_auto, minus workspace and workspace_bytes; the
+ * stream must belong to the current device.
+ */
+#define PA_STATIC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+int pa_decode_auto_static(const pa_kv_layout* layout, void* out, const void* q,
+                          int32_t num_reqs, int32_t num_q_heads, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                          const float* k_scale, const float* v_scale,
+                          const float* alibi_slopes, const pa_decode_plan* plan, void* stream);
 
 /*
  * Varlen (chunked) prefill over the paged cache (P2 §11.6: query_start_loc

@@ -23,6 +23,7 @@ __all__ = [
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
     "PaDecodePlan", "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
     "pa_decode_shared_prefix", "pa_decode_append", "pa_measure_read_stream", "EXPORTED_SYMBOLS",
+    "pa_decode_auto_static", "PA_STATIC_SCRATCH_BYTES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,9 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_HIP = -3
 PA_ERR_METADATA = -4
+PA_ERR_SCRATCH = -5
+# size of pa_decode_auto_static's device array (include/pa.h)
+PA_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024
 PA_CACHE_BF16 = 0
 PA_CACHE_FP8_E4M3 = 1
 
@@ -45,6 +49,7 @@ EXPORTED_SYMBOLS = (
     "pa_debug_gather_kv", "pa_debug_fp8_to_f32", "pa_debug_fp8_to_f16", "pa_validate_metadata",
     "pa_decode_plan_for", "pa_decode_auto", "pa_decode_partitioned_range",
     "pa_decode_shared_prefix", "pa_decode_append", "pa_measure_read_stream",
+    "pa_decode_auto_static",
     # host block manager (include/pa_blocks.h; binding in blocks.py)
     "pa_block_hashes", "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_usage",
     "pa_pool_ref_count", "pa_pool_lookup", "pa_pool_get_new_blocks", "pa_pool_touch",
@@ -117,6 +122,8 @@ def lib() -> ctypes.CDLL:
             "pa_decode_auto": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
                                 ctypes.POINTER(PaDecodePlan), _P, ctypes.c_size_t, _P], _I),
             "pa_validate_metadata": ([_P, _I, _P, _P, _I, _P, _I, _I, _I], _I),
+            "pa_decode_auto_static": ([lp, _P, _P, _I, _I, _P, _P, _P, _I, _P, _I, _F, _P, _P,
+                                       _P, ctypes.POINTER(PaDecodePlan), _P], _I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -335,6 +342,22 @@ def pa_decode_auto(layout, out, q, k_cache, v_cache, block_table, seq_lens, max_
         block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
         _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"),
         ctypes.byref(plan), _dev(workspace, "workspace"), nbytes, _stream()), "pa_decode_auto")
+
+
+def pa_decode_auto_static(layout, out, q, k_cache, v_cache, block_table, seq_lens,
+                          max_seq_len: int, scale: float, plan: PaDecodePlan, k_scale=None,
+                          v_scale=None, alibi_slopes=None) -> None:
+    """pa_decode_auto with the split path's partials in the library's static
+    device array (no workspace, nothing allocated)."""
+    _need(out, "out", torch.bfloat16)
+    _need_decode(layout, out, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                 alibi_slopes)
+    _check(lib().pa_decode_auto_static(
+        ctypes.byref(layout), _dev(out, "out"), _dev(q, "q"), q.shape[0], q.shape[1],
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(alibi_slopes, "alibi_slopes"),
+        ctypes.byref(plan), _stream()), "pa_decode_auto_static")
 
 
 def pa_decode_workspace_size(layout, num_reqs: int, num_q_heads: int) -> int:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -56,6 +57,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_HIP: return "HIP launch error";
     case PA_ERR_METADATA: return "inconsistent metadata";
+    case PA_ERR_SCRATCH: return "more scratch memory needed than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -403,24 +405,17 @@ int pa_decode_plan_for(const pa_kv_layout* layout, int32_t num_reqs, int32_t num
   return PA_OK;
 }
 
-int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
-                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
-                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                   int32_t max_seq_len, float scale, const float* k_scale, const float* v_scale,
-                   const float* alibi_slopes, const pa_decode_plan* plan, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  if (!plan) return PA_ERR_INVALID_ARG;
-  if (!plan->split)
-    return pa_decode(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
-                     bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale, alibi_slopes,
-                     stream);
-  PA_TRY(check_layout(layout));
-  if (num_reqs == 0) return PA_OK;
-  const size_t need = split_workspace_bytes(num_reqs, num_q_heads, layout->head_dim,
-                                            plan->max_num_partitions);
-  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need ||
-      !out || !aligned16(out))
-    return PA_ERR_INVALID_ARG;
+}  // extern "C"
+
+// The split path of a decode plan with its partials carved from `workspace`
+// (checked by the callers).
+static int decode_split_in(const pa_kv_layout* layout, void* out, const void* q,
+                           int32_t num_reqs, int32_t num_q_heads, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table, int32_t bt_stride,
+                           const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                           const float* k_scale, const float* v_scale,
+                           const float* alibi_slopes, const pa_decode_plan* plan,
+                           void* workspace, void* stream) {
   const size_t rows = (size_t)num_reqs * num_q_heads * plan->max_num_partitions;
   char* base = reinterpret_cast<char*>(workspace);
   float* tmp = reinterpret_cast<float*>(base);
@@ -434,6 +429,90 @@ int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t
   return pa_merge_partitions(out, tmp, ml, es, seq_lens, num_reqs, num_q_heads,
                              layout->head_dim, plan->partition_size, plan->max_num_partitions,
                              stream);
+}
+
+// Device memory of pa_decode_auto_static: the split-KV partials of a plan
+// live here instead of in a caller's workspace.  Every device the library
+// runs on holds its own copy, for the life of the process.  In host code
+// `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current, then kept).
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_auto(const pa_kv_layout* layout, void* out, const void* q, int32_t num_reqs,
+                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                   int32_t max_seq_len, float scale, const float* k_scale, const float* v_scale,
+                   const float* alibi_slopes, const pa_decode_plan* plan, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!plan) return PA_ERR_INVALID_ARG;
+  if (!plan->split)
+    return pa_decode(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                     bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale, alibi_slopes,
+                     stream);
+  PA_TRY(check_layout(layout));
+  if (num_reqs == 0) return PA_OK;
+  if (num_reqs < 0 || num_q_heads <= 0 || plan->max_num_partitions <= 0)
+    return PA_ERR_INVALID_ARG;
+  const size_t need = split_workspace_bytes(num_reqs, num_q_heads, layout->head_dim,
+                                            plan->max_num_partitions);
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need ||
+      !out || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  return decode_split_in(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                         bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                         alibi_slopes, plan, workspace, stream);
+}
+
+int pa_decode_auto_static(const pa_kv_layout* layout, void* out, const void* q,
+                          int32_t num_reqs, int32_t num_q_heads, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                          const float* k_scale, const float* v_scale,
+                          const float* alibi_slopes, const pa_decode_plan* plan, void* stream) {
+  if (!plan) return PA_ERR_INVALID_ARG;
+  if (!plan->split)
+    return pa_decode(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                     bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale, alibi_slopes,
+                     stream);
+  PA_TRY(check_layout(layout));
+  if (num_reqs == 0) return PA_OK;
+  if (num_reqs < 0 || num_q_heads <= 0 || plan->max_num_partitions <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!out || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  const size_t need = split_workspace_bytes(num_reqs, num_q_heads, layout->head_dim,
+                                            plan->max_num_partitions);
+  if (need > (size_t)PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  PA_TRY(scratch_address(&ws));
+  return decode_split_in(layout, out, q, num_reqs, num_q_heads, k_cache, v_cache, block_table,
+                         bt_stride, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                         alibi_slopes, plan, ws, stream);
 }
 
 int pa_prefill_varlen(const pa_kv_layout* layout, void* out, const void* q, int32_t num_tokens,

@@ -339,3 +339,26 @@ def test_binding_rejects_mismatched_partials():
              out=torch.zeros((R, H, D), dtype=torch.bfloat16), tmp_out=tmp.double(),
              max_logits=ml, exp_sums=torch.zeros((R, H, 3)),
              seq_lens=torch.ones(R, dtype=torch.int32), partition_size=16)
+
+
+def test_static_scratch_decode_rejects_plans_beyond_its_array():
+    """pa_decode_auto_static returns PA_ERR_SCRATCH, launching nothing, when
+    a split plan's partials exceed the static array (host check; no GPU)."""
+    L = pa.lib()
+    lay = pa.make_layout(100, 8, 128, 0)
+    p = ctypes.c_void_p(4096)
+    R, H = 8, 32
+    per = R * H * (128 + 2) * 4                          # bytes per partition of every row
+    pmax = pa.PA_STATIC_SCRATCH_BYTES // per + 2
+    plan = pa.PaDecodePlan(1, 16, pmax, 0, 0)
+    st = L.pa_decode_auto_static(ctypes.byref(lay), p, p, R, H, p, p, p, pmax, p, 16 * pmax,
+                                 0.1, None, None, None, ctypes.byref(plan), None)
+    assert st == pa.PA_ERR_SCRATCH
+    assert "static" in pa.pa_status_string(st)
+    # no plan, or a misaligned output: invalid argument
+    assert L.pa_decode_auto_static(ctypes.byref(lay), p, p, R, H, p, p, p, 4, p, 64, 0.1,
+                                   None, None, None, None, None) == pa.PA_ERR_INVALID_ARG
+    small = pa.PaDecodePlan(1, 16, 4, 0, 0)
+    assert L.pa_decode_auto_static(ctypes.byref(lay), ctypes.c_void_p(4097), p, R, H, p, p, p,
+                                   4, p, 64, 0.1, None, None, None, ctypes.byref(small),
+                                   None) == pa.PA_ERR_INVALID_ARG
