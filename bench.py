@@ -123,31 +123,76 @@ def traffic_for(kernel_key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The oracle as it stands, on the host cores, over whole passes of the
-    workload's decode (the sample: complete passes until ~budget_s)."""
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Threads the oracle may use: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when it is set (the host's CPU share)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def oracle_pass_rate(w, threads: int, reps: int = 3) -> dict:
+    """Median of `reps` whole passes of the oracle's decode over every request
+    and head of workload w, with the BLAS / OpenMP pools limited to
+    `threads`; rates from the bytes and tokens of those requests."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
     nbytes = decode_bytes(w)
-    t0 = time.perf_counter()
-    reqs_done = 0
-    while True:
-        for r in range(w.num_reqs):
-            oracle.decode(w, requests=[r])
-            reqs_done += 1
-            if time.perf_counter() - t0 > 30.0:
-                break
-        el = time.perf_counter() - t0
-        if el >= budget_s or el > 30.0:
-            break
-    dt = time.perf_counter() - t0
-    frac = reqs_done / w.num_reqs
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(nbytes["total"] * frac / dt / 1e9, 4), "unit": "GB/s",
-            "tokens_per_s": round(nbytes["tokens"] * frac / dt, 1),
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{reqs_done} request decodes ({frac:.2f} passes over all "
-                      f"{w.num_reqs} requests, all heads) in {dt:.1f} s, fp64 numpy"}
+    times = []
+    with threadpool_limits(limits=threads):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.decode(w)
+            times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    return {"threads": threads, "value": round(nbytes["total"] / med / 1e9, 4), "unit": "GB/s",
+            "kv_tokens_per_s": round(nbytes["tokens"] / med, 1),
+            "pass_s_median": round(med, 3), "pass_s": [round(t, 3) for t in times]}
+
+
+def cpu_baseline(w2, w3) -> dict:
+    """The oracle as it stands (numpy fp64), timed on the host's cores: the
+    median of three whole decode passes of the batched-decode workload and of
+    the long-context workload, at one thread and at every thread of the
+    host's share.  The headline value is the batched workload at all
+    threads."""
+    n_all = host_threads()
+    b1, ba = oracle_pass_rate(w2, 1), oracle_pass_rate(w2, n_all)
+    c1, ca = oracle_pass_rate(w3, 1), oracle_pass_rate(w3, n_all)
+    return {"value": ba["value"], "unit": "GB/s", "kv_tokens_per_s": ba["kv_tokens_per_s"],
+            "cores": n_all, "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": (f"whole decode passes (all {w2.num_reqs} requests and heads of the "
+                       f"batched-decode workload, {int(w2.seq_lens.sum())} KV tokens; all "
+                       f"{w3.num_reqs} x {int(w3.seq_lens[0])} tokens of the long-context "
+                       "workload), median of 3, fp64 numpy, at 1 thread and at "
+                       f"{n_all} threads"),
+            "threads_1": b1, "threads_all": ba,
+            "config3": {"workload": DESCR[3], "threads_1": c1, "threads_all": ca}}
+
+
+def library_record() -> dict:
+    """Which libpa.so this process loaded: its path and a hash of the file."""
+    import paged_kv_cache_77_amd as pa
+    path = pa.LIB_PATH
+    h = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    rel = os.path.relpath(path, ROOT)
+    return {"path": rel, "sha256": h, "from_env": bool(os.environ.get("PA_LIBRARY"))}
 
 
 def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
@@ -230,7 +275,7 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
     # pair around every single launch (the per-step figures above) also
     # charges the kernel for the two markers' dispatch gaps, ~5 us here,
     # which rocprofv3's kernel durations do not contain.
-    reps = max(steps, 20)
+    reps = max(steps, 300)       # long enough that the train's ends do not matter
     t_ev0 = torch.cuda.Event(enable_timing=True)
     t_ev1 = torch.cuda.Event(enable_timing=True)
     t_ev0.record(stream)
@@ -350,11 +395,8 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "algorithmic_flops_per_launch": flops,
-                        "vs_vector_alu_peak": round(tf / PEAK_VALU_DOT2_TFLOPS, 4),
                         "note": "f16 MFMA peak (= bf16); query heads padded to 16 per "
-                                "chunk on the MFMA N side are not counted; "
-                                "vs_vector_alu_peak: the same flops against the vector "
-                                "ALU's dot2 peak (the bound of the vector kernel)"}
+                                "chunk on the MFMA N side are not counted"}
         else:
             r["alu"] = {"bound": "alu", "kernel": r["kernel"], "achieved": round(tf, 2),
                         "peak": PEAK_VALU_DOT2_TFLOPS, "unit": "TFLOP/s",
@@ -537,9 +579,15 @@ def main() -> int:
     ceil = read_ceiling()
     ceil["roofline_achieved_over_ceiling"] = round(res["roofline"]["achieved"] / ceil["GBps"], 4)
     res["measured_read_ceiling"] = ceil
+    res["library"] = library_record()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
-        res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
+        from paged_kv_cache_77_amd import workloads as wl
+        w2 = w if args.config == 2 else wl.config_workload(2, poison=False)
+        w3 = wl.config_workload(3, poison=False)
+        res["cpu_baseline"] = cpu_baseline(w2, w3)
+        del w3
+        if args.config == 2:
+            res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
     if not args.no_other_workloads and args.config == 2:
         other = {}
         for cfg in (3, 4, 5):

@@ -18,10 +18,12 @@ BIG_BLOCKS = 140_000          # x 8 KV heads x 16 x 128 x bf16 = 4.59 GB per poo
 
 def _to_big_pool(d, w):
     """The same logical data with every used block moved to id BIG_BLOCKS-1-id
-    of a 4.59 GB pool (the rest of the pool is never read)."""
+    of a 4.59 GB pool.  Every other element of the pool holds bf16 NaN, as
+    the unused slots of the small pools do, so a stray read past 2^32 shows
+    up in the outputs instead of reading whatever the memory held."""
     shape = (BIG_BLOCKS,) + tuple(d.k_cache.shape[1:])
-    kb = torch.empty(shape, dtype=d.k_cache.dtype, device="cuda")
-    vb = torch.empty(shape, dtype=d.v_cache.dtype, device="cuda")
+    kb = torch.full(shape, float("nan"), dtype=d.k_cache.dtype, device="cuda")
+    vb = torch.full(shape, float("nan"), dtype=d.v_cache.dtype, device="cuda")
     used = np.unique(w.block_table[w.block_table >= 0])
     old = torch.from_numpy(used).long().cuda()
     new = BIG_BLOCKS - 1 - old
