@@ -63,14 +63,17 @@ def fp8_e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     pages only say FP8 K/V are loaded quantised and converted with a scale
     (P1 §3.2.1 / §3.2.4) and that FP8 storage takes one byte (P4 §2).
     """
-    c = np.asarray(codes).astype(np.int64)
+    # the closed form is evaluated once for each of the 256 codes; a code's
+    # value is then looked up (the same numbers, without re-deriving them for
+    # every element of a large cache)
+    c = np.arange(256, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = c & 0x7
     normal = sign * np.ldexp(1.0 + m / 8.0, e - 7)
     sub = sign * np.ldexp(m / 8.0, -6)
-    out = np.where(e == 0, sub, normal)
-    return np.where((e == 15) & (m == 7), np.nan, out)
+    value_of_code = np.where((e == 15) & (m == 7), np.nan, np.where(e == 0, sub, normal))
+    return value_of_code[np.asarray(codes).astype(np.uint8)]
 
 
 def cache_values(pool: np.ndarray, cache_dtype: str, scale: float = 1.0) -> np.ndarray:
