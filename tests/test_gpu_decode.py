@@ -7,6 +7,7 @@ import oracle
 from paged_kv_cache_77_amd import workloads as wl
 from paged_kv_cache_77_amd import device as dv
 import paged_kv_cache_77_amd as pa
+from tests import full_size as full
 from tests.parity import check_bf16, ulp_bf16
 
 pytestmark = pytest.mark.gpu
@@ -212,25 +213,21 @@ def test_decode_append(hq, hkv, d, cache, alibi):
     check_bf16(dv.bits_of(out), oracle.decode(w, k_pool=kp, v_pool=vp), "decode append")
 
 
-def test_decode_append_full_config2_sampled():
+def test_decode_append_full_config2():
     """The batched-decode workload's step as one call, in the benchmark's
-    launch configuration: pools bit-exact, sampled rows against the oracle."""
-    _announce("decode append, full config 2")
-    w = wl.config_workload(2)
+    launch configuration: pools and slots bit-exact, every request and head
+    against the oracle."""
+    _announce("decode append, full config 2, every row")
+    w = full.config(2)
     d = dv.to_device(w)
     sm = torch.empty((w.num_reqs,), dtype=torch.int64, device="cuda")
     out = _out(w)
     dv.run_decode_append(d, out, sm)
     torch.cuda.synchronize()
-    ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
+    ref_sm, kp, vp = full.after_write(2)
     assert np.array_equal(sm.cpu().numpy(), ref_sm)
-    kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
     assert np.array_equal(dv.bits_of(d.k_cache), kp) and np.array_equal(dv.bits_of(d.v_cache), vp)
-    rng = np.random.default_rng(22)
-    sample = sorted(set(rng.choice(w.num_reqs, size=6, replace=False).tolist())
-                    | {int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))})
-    ref = oracle.decode(w, k_pool=kp, v_pool=vp, requests=sample)
-    check_bf16(dv.bits_of(out)[sample], ref[sample], "config 2 append")
+    check_bf16(dv.bits_of(out), full.decode_ref(2), "config 2 append")
 
 
 def test_decode_empty_context_is_zero():
@@ -285,25 +282,17 @@ def test_decode_zero_query_is_mean():
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_full_size_config_sampled(cfg):
-    """Full-size configuration in the launch configuration the benchmark
-    times; the oracle computes a sample of requests (all heads)."""
-    _announce(f"full-size config {cfg}")
-    w = wl.config_workload(cfg)
+def test_full_size_config(cfg):
+    """Full-size configuration through split-KV + merge, the single pass and
+    the balanced decode; every request and head against the oracle."""
+    _announce(f"full-size config {cfg}, every row")
+    w = full.config(cfg)
     d = dv.to_device(w)
     if w.writes_new_kv:
         sm = torch.empty((w.num_tokens,), dtype=torch.int64, device="cuda")
         dv.write_new_kv(d, sm)
         torch.cuda.synchronize()
-        ref_sm = oracle.slot_mapping(w.block_table, w.query_start_loc, w.seq_lens, 16)
-        assert np.array_equal(sm.cpu().numpy(), ref_sm)
-        kp, vp = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.k_new, w.v_new, ref_sm, 16)
-    else:
-        kp, vp = w.k_pool, w.v_pool
-    rng = np.random.default_rng(cfg)
-    sample = sorted(set(rng.choice(w.num_reqs, size=min(6, w.num_reqs), replace=False).tolist())
-                    | {int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))})
-    ref = oracle.decode(w, k_pool=kp, v_pool=vp, requests=sample)
+        assert np.array_equal(sm.cpu().numpy(), full.after_write(cfg)[0])
     P = w.partition_size
     out = _out(w)
     dv.run_decode_partitioned(d, out, P)
@@ -312,9 +301,10 @@ def test_full_size_config_sampled(cfg):
     out2 = _out(w)
     dv.run_decode_balanced(d, out2)
     torch.cuda.synchronize()
-    check_bf16(dv.bits_of(out)[sample], ref[sample], f"config {cfg} split-KV")
-    check_bf16(dv.bits_of(out1)[sample], ref[sample], f"config {cfg} single pass")
-    check_bf16(dv.bits_of(out2)[sample], ref[sample], f"config {cfg} balanced")
+    ref = full.decode_ref(cfg)
+    check_bf16(dv.bits_of(out), ref, f"config {cfg} split-KV")
+    check_bf16(dv.bits_of(out1), ref, f"config {cfg} single pass")
+    check_bf16(dv.bits_of(out2), ref, f"config {cfg} balanced")
 
 
 def _shared_case(case):
@@ -372,20 +362,17 @@ def test_decode_shared_prefix(case):
     check_bf16(dv.bits_of(out), oracle.decode(w), f"shared prefix {case}")
 
 
-def test_decode_shared_prefix_full_config5_sampled():
+def test_decode_shared_prefix_full_config5():
     """The shared-prefix workload at full size (256 requests, 4096 shared
-    tokens, fp8) in the launch configuration the benchmark times."""
-    _announce("shared-prefix decode, full config 5")
-    w = wl.config_workload(5)
+    tokens, fp8) in the launch configuration the benchmark times; every
+    request and head against the oracle."""
+    _announce("shared-prefix decode, full config 5, every row")
+    w = full.config(5)
     d = dv.to_device(w)
     out = _out(w)
     dv.run_decode_shared_prefix(d, out, 256, 512)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(55)
-    sample = sorted(set(rng.choice(w.num_reqs, size=8, replace=False).tolist())
-                    | {0, w.num_reqs - 1, int(np.argmax(w.seq_lens))})
-    ref = oracle.decode(w, requests=sample)
-    check_bf16(dv.bits_of(out)[sample], ref[sample], "config 5 shared prefix")
+    check_bf16(dv.bits_of(out), full.decode_ref(5), "config 5 shared prefix")
 
 
 def test_balanced_workspace_reuse_and_all_units_written():

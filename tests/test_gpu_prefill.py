@@ -8,6 +8,7 @@ import torch
 import oracle
 from paged_kv_cache_77_amd import workloads as wl
 from paged_kv_cache_77_amd import device as dv
+from tests import full_size as full
 from tests.parity import check_bf16
 
 pytestmark = pytest.mark.gpu
@@ -134,20 +135,86 @@ def test_varlen_one_launch_batches(hq, hkv, d, prefill_first, alibi):
     check_bf16(got, oracle.prefill_varlen(w, k_pool=kp, v_pool=vp), "varlen one launch")
 
 
-def test_config4_full_size_sampled():
+def test_config4_full_size():
     """Full mixed batch (128 decode rows + 2048-token chunk on 6144 cached
-    tokens) in the benchmark's launch configuration; the oracle computes a
-    sample of rows."""
-    _announce("config 4 full size")
-    w = wl.config_workload(4)
-    got, kp, vp = _run(w)
-    rng = np.random.default_rng(4)
+    tokens) in the benchmark's launch configuration: the write's slots and
+    pools bit-exact, then every row and head -- the 128 decode rows and all
+    2048 rows of the chunk -- against the oracle."""
+    _announce("config 4 full size, every row")
+    w = full.config(4)
+    d = dv.to_device(w)
+    sm = torch.empty((w.num_tokens,), dtype=torch.int64, device="cuda")
+    dv.write_new_kv_fused(d, sm)
+    out = torch.full((w.num_tokens, w.num_q_heads, w.head_dim), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    dv.run_prefill(d, out)
+    torch.cuda.synchronize()
+    ref_sm, kp, vp = full.after_write(4)
+    assert np.array_equal(sm.cpu().numpy(), ref_sm)
+    assert np.array_equal(dv.bits_of(d.k_cache), kp) and np.array_equal(dv.bits_of(d.v_cache), vp)
+    del d
+    got = dv.bits_of(out)
+    ref = full.prefill_ref(4)
     pre = int(w.query_start_loc[-2])            # the prefill row's first token
-    toks = sorted(set(rng.integers(pre, w.num_tokens, size=24).tolist())
-                  | {pre, pre + 1, w.num_tokens - 1} | set(rng.integers(0, pre, 8).tolist()))
-    rows = [(t, h) for t in toks for h in range(w.num_q_heads)]
-    ref = oracle.prefill_varlen(w, rows=rows, k_pool=kp, v_pool=vp)
-    check_bf16(got[toks], ref[toks], "config 4 sampled rows")
+    check_bf16(got[:pre], ref[:pre], "config 4 decode rows")
+    check_bf16(got[pre:], ref[pre:], "config 4 prefill chunk")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_chunk_invariance_config4_shape(cache):
+    """A chunk resumes on the cached blocks of the earlier chunks and sees
+    exactly what an unchunked pass sees ("第11章 分块预填充与混合批处理"
+    §11.6; "vLLM 深度解析（二）" §5.2): at the mixed batch's chunk shape (32 q
+    / 8 KV heads, d 128), one 2048-token chunk on a 6144-token prefix against
+    the same tokens as two 1024-token chunks -- the first written to the
+    cache and computed on the 6144 prefix, the second written and computed on
+    the 7168 prefix.  Pools after both writes are bit-identical; both
+    outputs are within tolerance of the oracle and of each other."""
+    _announce(f"chunk invariance at the config-4 shape, {cache}")
+    w = wl.make_workload(name="t", seq_lens=[8192], q_lens=[2048], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, seed=88, cache_dtype=cache,
+                         bt_extra_cols=1)
+    def pools(d):
+        if cache == "bf16":
+            return dv.bits_of(d.k_cache), dv.bits_of(d.v_cache)
+        return d.k_cache.cpu().numpy(), d.v_cache.cpu().numpy()
+    shape = (2048, 32, 128)
+    # one chunk
+    d = dv.to_device(w)
+    sm = torch.empty((2048,), dtype=torch.int64, device="cuda")
+    dv.write_new_kv(d, sm)
+    whole = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    dv.run_prefill(d, whole)
+    torch.cuda.synchronize()
+    kp1, vp1 = pools(d)
+    del d
+    # two chunks over one set of pools
+    d = dv.to_device(w)
+    halves = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    for c, seq in ((0, 7168), (1, 8192)):
+        rows = slice(1024 * c, 1024 * (c + 1))
+        wc = dataclasses.replace(w, seq_lens=np.array([seq], np.int32),
+                                 q_lens=np.array([1024], np.int32),
+                                 query_start_loc=np.array([0, 1024], np.int32), q=w.q[rows],
+                                 k_new=w.k_new[rows], v_new=w.v_new[rows])
+        dc = dataclasses.replace(
+            d, w=wc, q=d.q[rows], k_new=d.k_new[rows], v_new=d.v_new[rows],
+            seq_lens=torch.tensor([seq], dtype=torch.int32, device="cuda"),
+            query_start_loc=torch.tensor([0, 1024], dtype=torch.int32, device="cuda"),
+            max_seq_len=seq, max_query_len=1024)
+        smc = torch.empty((1024,), dtype=torch.int64, device="cuda")
+        dv.write_new_kv(dc, smc)
+        dv.run_prefill(dc, halves[rows])
+        torch.cuda.synchronize()
+        assert np.array_equal(smc.cpu().numpy(), sm[rows].cpu().numpy())
+    kp2, vp2 = pools(d)
+    del d
+    assert np.array_equal(kp1, kp2) and np.array_equal(vp1, vp2)
+    ref = oracle.prefill_varlen(w, k_pool=kp1, v_pool=vp1)
+    g_whole, g_halves = dv.bits_of(whole), dv.bits_of(halves)
+    check_bf16(g_whole, ref, f"one chunk ({cache})")
+    check_bf16(g_halves, ref, f"two chunks ({cache})")
+    check_bf16(g_halves, oracle.bf16_bits_to_f64(g_whole), f"two chunks vs one ({cache})")
 
 
 @pytest.mark.parametrize("hq,hkv,d,cache", [(32, 8, 128, "bf16"), (28, 4, 128, "fp8"),
