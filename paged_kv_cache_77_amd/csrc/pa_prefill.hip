@@ -53,9 +53,14 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // v_mfma / ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane
 // i receives element i % 4 of the 64-bit values addressed by lanes
 // 4e + i / 4, e = 0..3 (a 4 x 4 transpose of 16-bit elements per group).
-__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
-  return __builtin_bit_cast(uint2, v);
+// Two of these reads form one 8-element MFMA operand (p0's elements first),
+// kept as one vector so both land in the operand's registers.
+__device__ __forceinline__ uint4 lds_read_tr16_pair(const void* p0, const void* p1) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(uint4, v);
 }
 
 constexpr int kBN = 64;         // keys per tile
@@ -88,9 +93,30 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
 
 template <int D>
 struct PrefillSmem {
-  uint4 k[2][kBN * D / 8];        // [key][16-byte chunk ^ (key & 15)]
-  uint4 vt[2][kBN * D / 8];       // V, the same layout (read transposed)
+  uint4 k[2][kBN * D / 8];        // [key][16-byte chunk ^ k_swizzle(key)]
+  uint4 vt[2][kBN * D / 8];       // [key][16-byte chunk ^ v_swizzle(key)] (read transposed)
 };
+
+// Position of 16-byte chunk c of tile row r is c ^ swizzle(r).  LDS has 64
+// four-byte banks: a 256-byte line is 16 chunks, one row at head size 128,
+// two rows at 64.
+// K rows are read as 16-byte fragments, 16 consecutive keys at one chunk
+// per 16 lanes: their chunks must fall in 16 different 4-bank groups, so
+// the swizzle is a bijection on the key's position among 16 (the row's line
+// half, r & 1, separates the two rows of a line at head size 64).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// V rows are read by the transposing 64-bit reads: 32 lanes take 4
+// consecutive rows x 4 consecutive chunks (64 bytes) at once, so each of the
+// 4 rows must put its 4 chunks in a different 4-chunk group (with the
+// key-only XOR of K all four rows land in one group: a 4-way bank conflict).
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // Work-group shape: hpw heads x qbw 32-query blocks (hpw * qbw == kWaves).
 __host__ __device__ inline void prefill_shape(int G, int& hpw, int& qbw, int& nhc) {
@@ -203,11 +229,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   // loop-invariant and computed once.
   constexpr int NCH = kBN * CH / (kWaves * 64);             // chunks per thread per tensor
   const int kc_chunk = tid % CH;
-  int k_key[NCH], k_lds[NCH];
+  int k_key[NCH], k_lds[NCH], v_lds[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     k_key[i] = tid / CH + (kWaves * 64 / CH) * i;
-    k_lds[i] = k_key[i] * CH + (kc_chunk ^ (k_key[i] & (CH - 1)));
+    k_lds[i] = k_key[i] * CH + (kc_chunk ^ k_swizzle<D>(k_key[i]));
+    v_lds[i] = k_key[i] * CH + (kc_chunk ^ v_swizzle<D>(k_key[i]));
   }
   // the raw codes stay in registers while the current tile is computed and
   // are converted to bf16 only when staged (converting at load time would
@@ -257,15 +284,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
     for (int j = 0; j < D / 32; ++j) {
       const int P = 64 * j + lane;
       const int key = P / CH;                               // key in the block
-      const int c = (P % CH) ^ ((kBlock * w + key) & (CH - 1));
-      const int64_t off = base + (int64_t)(key * D + c * 8) * EB;
+      const int ck = (P % CH) ^ k_swizzle<D>(kBlock * w + key);
+      const int cv = (P % CH) ^ v_swizzle<D>(kBlock * w + key);
+      const int64_t offk = base + (int64_t)(key * D + ck * 8) * EB;
+      const int64_t offv = base + (int64_t)(key * D + cv * 8) * EB;
       const int slot = kBlock * CH * w + 64 * j;
       // (destinations as plain LDS offsets: the copies' completion is
       // awaited explicitly before the barrier that publishes the buffer,
       // and the compiler then adds no wait before reads of the other one)
-      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void_t*)(uintptr_t)lds_offset(&sm.k[buf][slot]),
+      __builtin_amdgcn_global_load_lds(kbase + offk, (lds_void_t*)(uintptr_t)lds_offset(&sm.k[buf][slot]),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void_t*)(uintptr_t)lds_offset(&sm.vt[buf][slot]),
+      __builtin_amdgcn_global_load_lds(vbase + offv, (lds_void_t*)(uintptr_t)lds_offset(&sm.vt[buf][slot]),
                                        16, 0, 0);
     }
   };
@@ -290,7 +319,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       kl[k_lds[i]] = live[i] ? cvt8(kraw[i]) : make_uint4(0, 0, 0, 0);
-      vl[k_lds[i]] = live[i] ? cvt8(vraw[i]) : make_uint4(0, 0, 0, 0);
+      vl[v_lds[i]] = live[i] ? cvt8(vraw[i]) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -303,6 +332,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[b][v] = 0.f;
+
+  // Byte offsets in a V buffer of this lane's transposing reads, k-step 0:
+  // the V^T fragment of d block db (d = 32db + lane % 32) over keys
+  // 16ks + 4lh + 8(t/4) + t%4 for element t -- the order of P^T's k-step
+  // (b, s') = (ks/2, ks%2) -- comes from rows 4lh + gi/4 + 8hp (+16ks) of
+  // row-major V: lane gi of 16-lane group Gr addresses elements
+  // 32db + 16(Gr&1) + 4(gi%4) .. +3 of that row, and the transpose hands lane
+  // gi those rows' element 32db + 16(Gr&1) + gi.  Constant over the tiles.
+  uint32_t vt_off[DBLK][2];
+  {
+    const int Gr = lane / 16, gi = lane % 16;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        const int r = 4 * lh + gi / 4 + 8 * hp;
+        const int e0 = 32 * db + 16 * (Gr & 1) + 4 * (gi % 4);
+        vt_off[db][hp] = 16 * (r * CH + ((e0 / 8) ^ v_swizzle<D>(r))) + 2 * (e0 % 8);
+      }
+  }
 
   int32_t bid_next = -1;
   if constexpr (FP8) {
@@ -334,19 +383,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
       // -- S^T = K Q^T for the two 32-key halves of the tile
       // (the two halves' MFMA chains interleaved: consecutive MFMAs are
       // independent while the next K fragments are read)
+      // (K fragments read one k-step ahead of their products, two pairs
+      // in flight)
       f32x16_t s[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[b][v] = 0.f;
+      auto kread = [&](int k, int b) -> uint4 {
+        const int key = 32 * b + lq;
+        return sm.k[buf][key * CH + ((2 * k + lh) ^ k_swizzle<D>(key))];
+      };
+      uint4 kf[2][2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) kf[k][b] = kread(k, b);
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int key = 32 * b + lq;
-          const int c = 2 * k + lh;
-          const uint4 kf = sm.k[buf][key * CH + (c ^ (key & (CH - 1)))];
-          s[b] = mfma32(kf, qf[k], s[b]);
+        for (int b = 0; b < 2; ++b) s[b] = mfma32(kf[k & 1][b], qf[k], s[b]);
+        if (k + 2 < KSTEPS) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) kf[k & 1][b] = kread(k + 2, b);
         }
       }
       // -- ALiBi: s <- s * qk_scale + slope * (t - p_q)
@@ -407,34 +466,21 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             hw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-            l_run += bf16lo(hw[e]) + bf16hi(hw[e]);
+            l_run = dot2_bf16(hw[e], 0x3f803f80u, l_run);   // + both rounded weights
           }
           pf[2 * b + sp] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         }
       // -- O^T += V^T P^T
       {
-        // V^T fragment (d = 32db + lane % 32, keys 32b + 16s' + 4lh + 8(t/4)
-        // + t%4 for element t: the order of P^T's k-step (b, s')) from
-        // row-major V by two transposing reads.  Lane gi of 16-lane group G
-        // addresses row 32b + 16s' + 4lh + gi/4 (+8 for the second read),
-        // elements 32db + 16(G&1) + 4(gi%4) .. +3; the transpose hands lane
-        // gi of the group those rows' element 32db + 16(G&1) + gi.
-        const int G = lane / 16, gi = lane % 16;
+        // V^T fragments by two transposing reads each (offsets vt_off;
+        // k-step ks reads 16 rows further down)
         const char* vbuf = reinterpret_cast<const char*>(&sm.vt[buf][0]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {             // (d blocks' chains interleaved)
 #pragma unroll
           for (int db = 0; db < DBLK; ++db) {
-            const int r0 = 32 * (ks / 2) + 16 * (ks % 2) + 4 * lh + gi / 4;
-            const int e0 = 32 * db + 16 * (G & 1) + 4 * (gi % 4);
-            uint2 part[2];
-#pragma unroll
-            for (int hp = 0; hp < 2; ++hp) {
-              const int r = r0 + 8 * hp;
-              const int slot = r * CH + ((e0 / 8) ^ (r & (CH - 1)));
-              part[hp] = lds_read_tr16(vbuf + 16 * slot + 2 * (e0 % 8));
-            }
-            const uint4 vf = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+            const uint4 vf = lds_read_tr16_pair(vbuf + vt_off[db][0] + ks * (16 * D * 2),
+                                                vbuf + vt_off[db][1] + ks * (16 * D * 2));
             oacc[db] = mfma32(vf, pf[ks], oacc[db]);
           }
         }
