@@ -272,29 +272,41 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   // ---- bf16: direct copies.  Wave w copies block w of tile kt (16 keys, the
   // tile's keys 16w .. 16w+15) of K and V; instruction j writes LDS chunks
   // 64j .. 64j+63 of the block, lane i chunk 64j + i, fetching the global
-  // chunk that the swizzle puts there.
+  // chunk that the swizzle puts there.  The block's address is wave-uniform
+  // (scalar registers); each lane adds its 32-bit offset in the block.  (The
+  // block id is a vector load made uniform when used: a scalar load would
+  // share the LDS reads' wait counter and, returning out of order, force
+  // full waits on it.)
   auto block_id = [&](int kt) -> int32_t {                  // wave-uniform
     return kt * kBN + kBlock * w < seq_len ? bt_row[kt * 4 + w] : -1;
   };
-  auto dma = [&](int kt, int32_t bid, int buf) {
+
+  uint32_t dma_k[D / 32], dma_v[D / 32];                    // lane byte offsets in a block
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int P = 64 * j + lane;
+    const int key = P / CH;                                 // key in the block
+    dma_k[j] = (uint32_t)((key * D + ((P % CH) ^ k_swizzle<D>(kBlock * w + key)) * 8) * EB);
+    dma_v[j] = (uint32_t)((key * D + ((P % CH) ^ v_swizzle<D>(kBlock * w + key)) * 8) * EB);
+  }
+  auto dma = [&](int kt, int32_t bid_v, int buf) {
     (void)kt;
+    const int32_t bid = __builtin_amdgcn_readfirstlane(bid_v);
     if (bid < 0) return;                                    // block past the context
     const int64_t base = ((int64_t)bid * blk_stride + head_off) * EB;
+    const uint8_t* kblk = kbase + base;
+    const uint8_t* vblk = vbase + base;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-      const int P = 64 * j + lane;
-      const int key = P / CH;                               // key in the block
-      const int ck = (P % CH) ^ k_swizzle<D>(kBlock * w + key);
-      const int cv = (P % CH) ^ v_swizzle<D>(kBlock * w + key);
-      const int64_t offk = base + (int64_t)(key * D + ck * 8) * EB;
-      const int64_t offv = base + (int64_t)(key * D + cv * 8) * EB;
       const int slot = kBlock * CH * w + 64 * j;
       // (destinations as plain LDS offsets: the copies' completion is
       // awaited explicitly before the barrier that publishes the buffer,
       // and the compiler then adds no wait before reads of the other one)
-      __builtin_amdgcn_global_load_lds(kbase + offk, (lds_void_t*)(uintptr_t)lds_offset(&sm.k[buf][slot]),
+      __builtin_amdgcn_global_load_lds((const void*)(kblk + dma_k[j]),
+                                       (lds_void_t*)(uintptr_t)lds_offset(&sm.k[buf][slot]),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + offv, (lds_void_t*)(uintptr_t)lds_offset(&sm.vt[buf][slot]),
+      __builtin_amdgcn_global_load_lds((const void*)(vblk + dma_v[j]),
+                                       (lds_void_t*)(uintptr_t)lds_offset(&sm.vt[buf][slot]),
                                        16, 0, 0);
     }
   };
@@ -353,14 +365,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
       }
   }
 
-  int32_t bid_next = -1;
+  int32_t bid_next = -1;                     // the block id of tile kt + 1
   if constexpr (FP8) {
     fetch(kt_begin, tile_bids(kt_begin));
     bid_next = tile_bids(kt_begin + 1);
     stage(0);
   } else {
-    dma(kt_begin, block_id(kt_begin), 0);
     if (kt_begin + 1 < n_tiles) bid_next = block_id(kt_begin + 1);
+    dma(kt_begin, block_id(kt_begin), 0);
     wait_copies();
     zero_tail(kt_begin, 0);
   }
@@ -369,23 +381,21 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
   for (int kt = kt_begin; kt < n_tiles; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < n_tiles;
-    if (more) {
-      if constexpr (FP8) {
+    if constexpr (FP8) {
+      if (more) {
         fetch(kt + 1, bid_next);
         bid_next = tile_bids(kt + 2);
-      } else {
-        dma(kt + 1, bid_next, buf ^ 1);
-        if (kt + 2 < n_tiles) bid_next = block_id(kt + 2);
       }
     }
     const int k0 = kt * kBN;
-    if (k0 <= wave_pmax) {                      // some key of the tile is visible to the wave
+    const bool compute = k0 <= wave_pmax;       // some key of the tile is visible to the wave
+    f32x16_t s[2];
+    if (compute) {
       // -- S^T = K Q^T for the two 32-key halves of the tile
       // (the two halves' MFMA chains interleaved: consecutive MFMAs are
       // independent while the next K fragments are read)
       // (K fragments read one k-step ahead of their products, two pairs
       // in flight)
-      f32x16_t s[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -408,6 +418,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
           for (int b = 0; b < 2; ++b) kf[k & 1][b] = kread(k + 2, b);
         }
       }
+      // keep that order: 4 reads, then (2 products, 2 reads) per k-step
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k + 2 < KSTEPS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    // bf16: the next tile's copy, issued by every wave (each copies its own
+    // block) after this tile's QK products: while a copy is in flight the
+    // compiler waits for all outstanding LDS reads at once, which the QK
+    // fragment reads, one k-step ahead, cannot afford
+    if constexpr (!FP8) {
+      if (more) {
+        dma(kt + 1, bid_next, buf ^ 1);
+        if (kt + 2 < n_tiles) bid_next = block_id(kt + 2);
+      }
+    }
+    if (compute) {
       // -- ALiBi: s <- s * qk_scale + slope * (t - p_q)
       if constexpr (ALIBI) {
         const float bias0 = slope * (float)(k0 + 4 * lh - p_q);
@@ -557,7 +587,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PrefillSmem<D
 // work-group; with snake, its j-th item is j * stride + first for even j and
 // (j + 1) * stride - 1 - first for odd j (persistent workers then pair the
 // long query tiles of a causal chunk with the short ones).
-template <int D, bool FP8, bool ALIBI>
+// With DIRECT, the work-group's one item is (request blockIdx.y, tile
+// blockIdx.x / U, group blockIdx.x % U) instead.
+template <int D, bool FP8, bool ALIBI, bool DIRECT = false>
 __device__ __forceinline__ void prefill_items(const PrefillArgs& a, PrefillSmem<D>& sm,
                                               int* sched, int64_t first, int64_t stride,
                                               int64_t num_items, bool snake) {
@@ -568,6 +600,13 @@ __device__ __forceinline__ void prefill_items(const PrefillArgs& a, PrefillSmem<
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   for (int64_t j = 0;; ++j) {
     const int64_t k = (snake && (j & 1)) ? (j + 1) * stride - 1 - first : j * stride + first;
+    if constexpr (DIRECT) {
+      const int r = blockIdx.y, tile = blockIdx.x / U;
+      const int q_len = a.query_start_loc[r + 1] - a.query_start_loc[r];
+      if (j > 0 || q_len <= 1 || tile * QT >= q_len) break;
+      prefill_item<D, FP8, ALIBI>(a, sm, r, tile, blockIdx.x % U);
+      continue;
+    }
     if (k >= num_items) break;
     const int64_t kt = k / U;
     if (w == 0) {
@@ -621,24 +660,12 @@ __device__ __forceinline__ void prefill_items(const PrefillArgs& a, PrefillSmem<
 // the tile count (decode rows cost no work-groups).
 // With direct != 0 (few requests) the grid is (tiles * U, num_reqs) instead:
 // one item per work-group, request blockIdx.y, no search.
-template <int D, bool FP8, bool ALIBI>
+template <int D, bool FP8, bool ALIBI, bool DIRECT>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillArgs a,
-                                                                 int64_t num_items,
-                                                                 int direct) {
+                                                                 int64_t num_items) {
   __shared__ PrefillSmem<D> sm;
   __shared__ int sched[2];
-  if (direct) {
-    int hpw, qbw, nhc;
-    prefill_shape(a.num_q_heads / a.num_kv_heads, hpw, qbw, nhc);
-    const int U = a.num_kv_heads * nhc;
-    const int QT = kQW * qbw;
-    const int r = blockIdx.y, tile = blockIdx.x / U;
-    const int q_len = a.query_start_loc[r + 1] - a.query_start_loc[r];
-    if (q_len <= 1 || tile * QT >= q_len) return;
-    prefill_item<D, FP8, ALIBI>(a, sm, r, tile, blockIdx.x % U);
-    return;
-  }
-  prefill_items<D, FP8, ALIBI>(a, sm, sched, blockIdx.x, gridDim.x, num_items, false);
+  prefill_items<D, FP8, ALIBI, DIRECT>(a, sm, sched, blockIdx.x, gridDim.x, num_items, false);
 }
 
 // Shared-prefix partials: work-group (query block of 128 flattened decode
@@ -721,9 +748,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (direct) grid = dim3((unsigned)(per_req * a.num_kv_heads * nhc), a.num_reqs);
   const bool fp8 = a.cache_dtype != 0;
   const bool alibi = a.alibi_slopes != nullptr;
-#define PA_PREFILL(DV, F8, AL) \
-  hipLaunchKernelGGL((prefill_kernel<DV, F8, AL>), grid, dim3(kWaves * 64), 0, st, a, num_items, \
-                     direct)
+#define PA_PREFILL(DV, F8, AL)                                                              \
+  do {                                                                                      \
+    if (direct)                                                                             \
+      hipLaunchKernelGGL((prefill_kernel<DV, F8, AL, true>), grid, dim3(kWaves * 64), 0, st, a, \
+                         num_items);                                                        \
+    else                                                                                    \
+      hipLaunchKernelGGL((prefill_kernel<DV, F8, AL, false>), grid, dim3(kWaves * 64), 0, st,   \
+                         a, num_items);                                                     \
+  } while (0)
   if (a.head_dim == 64) {
     if (fp8) {
       if (alibi) PA_PREFILL(64, true, true); else PA_PREFILL(64, true, false);
