@@ -36,31 +36,63 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
   // the rest ranks R - 1 - (z - lpt_half), so the work-group that joins a
   // compute unit later takes a short unit beside a long one.
   int r = blockIdx.z;
+  int unit = blockIdx.y;
   if constexpr (!PART) {
     if (a.lpt) {
       const int R = a.num_reqs;
-      // with a.lpt_half > 0 the requests from a.lpt_half on take the
-      // remaining ranks backwards, so the second round's work-groups pair
-      // the shortest units with the longest
       const int z = blockIdx.z, hf = a.lpt_half;
-      const int target = (hf > 0 && z >= hf) ? R - 1 - (z - hf) : z;
-      for (int i = threadIdx.x; i < R; i += WAVES * kWave) sm.bt[i] = a.seq_lens[i];
+      int32_t* len = sm.bt;                 // [R] context lengths
+      int32_t* req_of = sm.bt + R;          // [R] request of each rank
+      for (int i = threadIdx.x; i < R; i += WAVES * kWave) len[i] = a.seq_lens[i];
       __syncthreads();
       for (int j = threadIdx.x; j < R; j += WAVES * kWave) {
-        const int lj = sm.bt[j];
+        const int lj = len[j];
         int rank = 0;
         for (int k = 0; k < R; ++k) {
-          const int lk = sm.bt[k];
+          const int lk = len[k];
           rank += (lk > lj || (lk == lj && k < j)) ? 1 : 0;
         }
-        if (rank == target) sm.sched = j;
+        req_of[rank] = j;
       }
       __syncthreads();
-      r = __builtin_amdgcn_readfirstlane(sm.sched);
+      // Work-groups reach the XCDs round-robin (slot L on XCD L % 8) and, in
+      // the two-round grid, slots z and z + hf of an XCD share a compute
+      // unit, which thus streams the pair of ranks (p, R - 1 - p).  On
+      // MI355X the odd XCDs stream about 7% slower than the even ones on
+      // equal work, so when the (KV head, chunk) units are exactly 8 (one
+      // per XCD in grid order) the pairs are ranked by their token sum and
+      // the heavier half goes to the even XCDs, the lighter half to the odd
+      // ones: slot (XCD x, unit slot s = z % hf, round z / hf) takes pair
+      // q = (x & 1) * hf/2 + s % (hf/2) in that order and the (KV head, chunk)
+      // unit 2 (x >> 1) + s / (hf/2).  Each (rank, unit) is taken once.
+      const bool xcd_weighted = PA_DECODE_XCD_WEIGHT && hf > 0 && R == 2 * hf && hf % 2 == 0 &&
+                                gridDim.x == 1 && gridDim.y == 8;
+      int target;
+      if (xcd_weighted) {
+        int32_t* psum = sm.bt + 2 * R;      // [hf] token sums of the rank pairs
+        int32_t* pair_at = sm.bt + 2 * R + hf;   // [hf] pairs, heaviest first
+        for (int p = threadIdx.x; p < hf; p += WAVES * kWave)
+          psum[p] = len[req_of[p]] + len[req_of[R - 1 - p]];
+        __syncthreads();
+        for (int p = threadIdx.x; p < hf; p += WAVES * kWave) {
+          int pos = 0;
+          for (int k = 0; k < hf; ++k) pos += (psum[k] > psum[p] || (psum[k] == psum[p] && k < p));
+          pair_at[pos] = p;
+        }
+        __syncthreads();
+        const int x = blockIdx.y, half = hf / 2, sl = z % hf;
+        const int pr = pair_at[(x & 1) * half + sl % half];
+        target = z < hf ? pr : R - 1 - pr;
+        unit = 2 * (x >> 1) + sl / half;
+      } else {
+        target = (hf > 0 && z >= hf) ? R - 1 - (z - hf) : z;
+      }
+      r = __builtin_amdgcn_readfirstlane(req_of[target]);
+      unit = __builtin_amdgcn_readfirstlane(unit);
       __syncthreads();
     }
   }
-  decode_unit<D, GC, FP8, WAVES, PART, PD>(a, sm, r, blockIdx.y, blockIdx.x, n_chunks);
+  decode_unit<D, GC, FP8, WAVES, PART, PD>(a, sm, r, unit, blockIdx.x, n_chunks);
 }
 
 // ---------------------------------------------------------------------------

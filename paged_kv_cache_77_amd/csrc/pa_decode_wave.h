@@ -75,6 +75,11 @@ constexpr float kTau = 8.0f;
 #endif
 // Longest-first order of the single pass's work-groups (0 disables), used for
 // batches of up to kLptMaxReqs requests.
+// Two-round single pass with exactly 8 (KV head, chunk) units: heavier
+// work-group pairs on the even XCDs (see decode_kernel).
+#ifndef PA_DECODE_XCD_WEIGHT
+#define PA_DECODE_XCD_WEIGHT 1
+#endif
 #ifndef PA_DECODE_LPT
 #define PA_DECODE_LPT 1
 #endif
