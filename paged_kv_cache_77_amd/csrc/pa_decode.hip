@@ -37,6 +37,31 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
   // compute unit later takes a short unit beside a long one.
   int r = blockIdx.z;
   int unit = blockIdx.y;
+  int part_idx = blockIdx.x;
+  if constexpr (PART) {
+    // Split-KV over a grid of many rounds: every XCD gets the same number of
+    // work-groups in dispatch order (slot L on XCD L % 8), but the odd XCDs
+    // stream ~7% slower, so the items (partition, unit, request) are dealt
+    // unevenly -- xcd_even to each even XCD, xcd_odd to each odd one, the odd
+    // XCDs' surplus slots idle.
+    if (a.xcd_items > 0) {
+      const int L = blockIdx.x, x = L % 8, j = L / 8;
+      int item;
+      if ((x & 1) == 0) {
+        item = j < a.xcd_even ? (x >> 1) * a.xcd_even + j : -1;
+      } else {
+        const int base = 4 * a.xcd_even + (x >> 1) * a.xcd_odd;
+        item = (j < a.xcd_odd && base + j < a.xcd_items) ? base + j : -1;
+      }
+      if (item < 0) return;
+      const int per_req = a.num_kv_heads * n_chunks;      // units per request
+      const int nparts = a.xcd_items / (a.num_reqs * per_req);
+      r = item / (per_req * nparts);
+      const int rem = item - r * per_req * nparts;
+      unit = rem / nparts;
+      part_idx = rem - unit * nparts;
+    }
+  }
   if constexpr (!PART) {
     if (a.lpt) {
       const int R = a.num_reqs;
@@ -92,7 +117,7 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
       __syncthreads();
     }
   }
-  decode_unit<D, GC, FP8, WAVES, PART, PD>(a, sm, r, unit, blockIdx.x, n_chunks);
+  decode_unit<D, GC, FP8, WAVES, PART, PD>(a, sm, r, unit, part_idx, n_chunks);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,8 +583,21 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     if (a.part_end > 0) nparts = min(nparts, a.part_end) - a.part_begin;
     if (nparts <= 0) return hipSuccess;
     dim3 grid(nparts, a.num_kv_heads * n_chunks, a.num_reqs);
+    DecodeArgs b = a;
+    b.xcd_items = 0;
+    const int64_t items = (int64_t)grid.x * grid.y * grid.z;
+    const int cus = device_cu_count();
+    if (PA_DECODE_XCD_WEIGHT && cus > 0 && items >= 8 * (int64_t)cus && items < (1 << 28)) {
+      // even : odd XCD shares 1.07 : 1 (measured streaming rates)
+      const int64_t ne = (items * 107 + 4 * 207 - 1) / (4 * 207);
+      const int64_t no = (items - 4 * ne + 3) / 4;
+      b.xcd_items = (int32_t)items;
+      b.xcd_even = (int32_t)ne;
+      b.xcd_odd = (int32_t)no;
+      grid = dim3((unsigned)(8 * std::max(ne, no)), 1, 1);
+    }
     hipLaunchKernelGGL((decode_kernel<D, GC, FP8, WAVES, true, PD>), grid, dim3(WAVES * 64), 0, st,
-                       a, n_chunks);
+                       b, n_chunks);
   } else {
     // Few work-groups: spread each context over more waves; many: more groups.
     dim3 grid(1, a.num_kv_heads * n_chunks, a.num_reqs);

@@ -33,6 +33,8 @@ struct DecodeArgs {
   int32_t open_last;                // partition part_end - 1 runs to seq_len (a tail record)
   int32_t lpt;                      // set by the launcher: longest requests first
   int32_t lpt_half;                 // set by the launcher: > 0 pairs ranks (see decode_kernel)
+  int32_t xcd_items;                // set by the launcher (split-KV): > 0 = 1-D grid of that many
+  int32_t xcd_even, xcd_odd;        //   items, xcd_even per even XCD, xcd_odd per odd one
   float scale;
 };
 
