@@ -390,7 +390,9 @@ def measure(cfg: int, path: str, partition_size: int, steps: int, warmup: int,
         G = w.num_q_heads // w.num_kv_heads
         flops = 4 * G * w.head_dim * nbytes["tokens"] * w.num_kv_heads
         tf = flops / (kern_ms * 1e-3) / 1e12
-        if decode_kernel_name(w) == "decode_mfma_kernel" or path == "shared":
+        on_mfma = path == "shared" or (path != "balanced" and
+                                        decode_kernel_name(w) == "decode_mfma_kernel")
+        if on_mfma:
             r["alu"] = {"bound": "mfma", "kernel": r["kernel"], "achieved": round(tf, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -597,6 +599,11 @@ def main() -> int:
         # the shared-prefix workload through the per-request decode (pa_decode)
         o = measure(5, "single", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
         other["config5_per_request_decode"] = summary(o)
+        del o
+        # the same workload on the vector-ALU kernel (the work-balanced decode
+        # always runs there): the A/B for the matrix-core decode of FP8 caches
+        o = measure(5, "balanced", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
+        other["config5_vector_alu_decode"] = summary(o)
         del o
         # the batched-decode step as two launches (write, then pa_decode)
         o = measure(2, "single", 0, max(10, args.steps // 2), max(3, args.warmup // 2))
