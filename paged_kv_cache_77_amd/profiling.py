@@ -56,8 +56,8 @@ RUNS = {
         # matrix-core counters (derived metrics of rocprofv3): MfmaUtil = the
         # share of SIMD cycles the MFMA pipe was busy, MfmaFlopsBF16 = bf16
         # MFMA flops executed
-        "mfma": {"counters": ["MfmaUtil", "MfmaFlopsBF16"],
-                 "kernels": ["pa::prefill_kernel", "pa::varlen_kernel"]},
+        "counters": {"counters": ["MfmaUtil", "MfmaFlopsBF16"],
+                     "kernels": ["pa::prefill_kernel", "pa::varlen_kernel"]},
     },
     "shared_prefix_fp8": {
         "title": "shared-prefix fp8 decode: 256 requests sharing 256 blocks (4096 tokens) + "
@@ -67,14 +67,25 @@ RUNS = {
         "args": "--config 5",
         "keys": {"config5_shared": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel",
                                     "pa::merge_few_kernel"]},
-        "mfma": {"counters": ["MfmaUtil", "MfmaFlopsBF16", "MfmaFlopsF16"],
-                 "kernels": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel"]},
+        "counters": {"counters": ["MfmaUtil", "MfmaFlopsBF16", "MfmaFlopsF16"],
+                     "kernels": ["pa::shared_prefix_kernel", "pa::decode_mfma_kernel"]},
     },
     "shared_prefix_fp8_per_request": {
         "title": "the same workload through the per-request decode (pa_decode, matrix-core "
                  "kernel)",
         "args": "--config 5 --path single",
         "keys": {"config5_single": ["pa::decode_mfma_kernel"]},
+    },
+    "shared_prefix_fp8_vector_alu": {
+        "title": "the same workload on the vector-ALU kernel (the work-balanced decode, which "
+                 "always runs there): the A/B for the matrix-core decode of FP8 caches",
+        "args": "--config 5 --path balanced",
+        "keys": {"config5_balanced": ["pa::decode_balanced_kernel",
+                                      "pa::balanced_merge_kernel"]},
+        # VALUBusy = % of the time the vector ALUs were busy
+        "counters": {"counters": ["VALUBusy"], "kernels": ["pa::decode_balanced_kernel"],
+                     "what": "vector-ALU counter per dispatch (median over the group): "
+                             "VALUBusy = % of the time the vector ALUs were busy"},
     },
 }
 
@@ -90,9 +101,9 @@ def commands(outdir: str = "rocprof_out") -> list:
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             cmds.append(f"rocprofv3 --pmc {c} -d {outdir} -o {c.lower()}_{name} -- "
                         f"{BENCH} {r['args']} --steps 3 --warmup 1")
-        if "mfma" in r:
-            cmds.append(f"rocprofv3 --pmc {' '.join(r['mfma']['counters'])} -d {outdir} "
-                        f"-o mfma_{name} -- {BENCH} {r['args']} --steps 3 --warmup 1")
+        if "counters" in r:
+            cmds.append(f"rocprofv3 --pmc {' '.join(r['counters']['counters'])} -d {outdir} "
+                        f"-o counters_{name} -- {BENCH} {r['args']} --steps 3 --warmup 1")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(f"rocprofv3 --pmc {c} -d {outdir} -o {c.lower()}_copy -- "
                     f"python3 bench.py --copy-calibration")
@@ -209,13 +220,14 @@ def summarize(outdir: str = "rocprof_out", profiles: str = "profiles") -> dict:
             traffic[key] = {"bytes_per_launch": int(round(tot)), "kernel_sha": sha,
                             "kernels": prefixes}
             lines.append(f"# {key}: HBM traffic {tot / 1e6:.2f} MB per launch")
-        if "mfma" in r:
-            db = os.path.join(outdir, f"mfma_{name}_results.db")
-            lines.append("# matrix-core counters per dispatch (median over the group): "
-                         "MfmaUtil = % of SIMD cycles the MFMA pipe was busy, "
-                         "MfmaFlopsBF16 = bf16 MFMA flops executed")
-            vals = {c: _per_dispatch(db, c) for c in r["mfma"]["counters"]}
-            for pfx in r["mfma"]["kernels"]:
+        if "counters" in r:
+            db = os.path.join(outdir, f"counters_{name}_results.db")
+            lines.append("# " + r["counters"].get(
+                "what", "matrix-core counters per dispatch (median over the group): "
+                        "MfmaUtil = % of SIMD cycles the MFMA pipe was busy, "
+                        "MfmaFlopsBF16 = bf16 MFMA flops executed"))
+            vals = {c: _per_dispatch(db, c) for c in r["counters"]["counters"]}
+            for pfx in r["counters"]["kernels"]:
                 parts = []
                 for c, g in vals.items():
                     k = _dominant(g, pfx)
