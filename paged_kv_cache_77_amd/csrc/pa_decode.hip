@@ -68,7 +68,11 @@ __global__ __launch_bounds__(WAVES * 64, (decode_min_waves<GC, FP8, PART, WAVES>
       const int z = blockIdx.z, hf = a.lpt_half;
       int32_t* len = sm.bt;                 // [R] context lengths
       int32_t* req_of = sm.bt + R;          // [R] request of each rank
-      for (int i = threadIdx.x; i < R; i += WAVES * kWave) len[i] = a.seq_lens[i];
+      // (in a varlen batch only rows with q_len 1 are decode rows: the
+      // others rank last, and their work-groups exit)
+      for (int i = threadIdx.x; i < R; i += WAVES * kWave)
+        len[i] = (a.query_start_loc == nullptr ||
+                  a.query_start_loc[i + 1] - a.query_start_loc[i] == 1) ? a.seq_lens[i] : -1;
       __syncthreads();
       for (int j = threadIdx.x; j < R; j += WAVES * kWave) {
         const int lj = len[j];
@@ -604,7 +608,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool partitioned, hipStre
     const int64_t groups = (int64_t)grid.y * grid.z;
     DecodeArgs b = a;
     // (the rank search costs O(num_reqs) per thread: kept to modest batches)
-    b.lpt = (PA_DECODE_LPT && a.query_start_loc == nullptr && a.num_reqs <= kLptMaxReqs) ? 1 : 0;
+    b.lpt = (PA_DECODE_LPT && a.num_reqs <= kLptMaxReqs) ? 1 : 0;
     const int64_t min_len = groups < 384 ? PA_DECODE_WAVES_SINGLE_MIN_LEN
                                          : 2 * PA_DECODE_WAVES_SINGLE_MIN_LEN;
     const int cus = device_cu_count();

@@ -454,7 +454,11 @@ __global__ __launch_bounds__(kMWaves * 64, FP8 ? (ALIBI ? 3 : PA_MFMA_MINW_FP8) 
   if constexpr (!PART) {
     if (a.lpt) {
       const int R = a.num_reqs;
-      for (int i = threadIdx.x; i < R; i += kMWaves * kWave) sm.bt[i] = a.seq_lens[i];
+      // (in a varlen batch only rows with q_len 1 are decode rows: the
+      // others rank last, and their work-groups exit)
+      for (int i = threadIdx.x; i < R; i += kMWaves * kWave)
+        sm.bt[i] = (a.query_start_loc == nullptr ||
+                    a.query_start_loc[i + 1] - a.query_start_loc[i] == 1) ? a.seq_lens[i] : -1;
       __syncthreads();
       for (int j = threadIdx.x; j < R; j += kMWaves * kWave) {
         const int lj = sm.bt[j];
@@ -609,7 +613,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, bool partitioned, hipStream_t
   // (rank search: O(num_reqs) per thread, so modest batches only; the
   // rank buffer is the block-table staging array)
   static_assert(kMaxLptReqs <= kMBtChunk, "rank buffer");
-  b.lpt = (!partitioned && a.query_start_loc == nullptr && a.num_reqs <= kMaxLptReqs) ? 1 : 0;
+  b.lpt = (!partitioned && a.num_reqs <= kMaxLptReqs) ? 1 : 0;
 #define PA_MFMA(DV, PT, AL) \
   do {                                                                                        \
     if (fp8)                                                                                  \
